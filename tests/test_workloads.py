@@ -1,0 +1,79 @@
+"""The seeded input generator: shapes, the position code, rounding, stability."""
+import numpy as np
+import torch
+
+from workloads import (CONFIGS, Workload, digest, make_qkv, make_qkv_sequence,
+                       position_code, round_like, to_bf16_bits)
+
+
+def test_config_shapes():
+    assert CONFIGS["tiny"].N == 1024
+    assert CONFIGS["wan1p3b_480p"].N == 32760
+    assert CONFIGS["wan14b_720p"].N == 75600
+    assert CONFIGS["hunyuan_720p"].N == 119056
+    assert CONFIGS["stress_1pct"].N == 75600 and CONFIGS["stress_1pct"].n_clusters == 16
+    for wl in CONFIGS.values():
+        assert (wl.N - wl.n_text) % wl.kv_block == 0
+
+
+def test_position_code_norm_and_split():
+    for d in (64, 128):
+        pe = position_code((3, 5, 7), d)
+        # every sin/cos pair has unit norm: |PE|^2 = d/2 for every token
+        np.testing.assert_allclose((pe ** 2).sum(1), d / 2, rtol=1e-12)
+    pe = position_code((3, 5, 7), 128)
+    # the first 44 dims depend on t only, the next 42 on y only, the last 42 on x only
+    g = pe.reshape(3, 5, 7, 128)
+    assert np.allclose(g[:, :1, :1, :44], g[:, :, :, :44])
+    assert np.allclose(g[:1, :, :1, 44:86], g[:, :, :, 44:86])
+    assert np.allclose(g[:1, :1, :, 86:], g[:, :, :, 86:])
+    # position 0 of each axis: sin 0 = 0, cos 0 = 1
+    np.testing.assert_array_equal(pe[0, :22], 0.0)
+    np.testing.assert_array_equal(pe[0, 22:44], 1.0)
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
+    x[:4] = [0.0, -0.0, np.inf, -np.inf]
+    ours = to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_generator_is_seeded_and_stable():
+    wl = CONFIGS["tiny"]
+    q, k, v = make_qkv(wl)
+    q2, k2, v2 = make_qkv(wl)
+    assert digest(q, k, v) == digest(q2, k2, v2)
+    assert q.shape == (1, 2, 1024, 64) and q.dtype == np.float32
+    # the first H' heads do not depend on how many heads are generated
+    q1, k1, v1 = make_qkv(wl, heads=1)
+    np.testing.assert_array_equal(q1[0, 0], q[0, 0])
+    np.testing.assert_array_equal(v1[0, 0], v[0, 0])
+    # pinned digest of the tiny workload (input-stability pin)
+    assert digest(q, k, v) == TINY_DIGEST
+
+
+def test_bf16_workload_and_text_tokens():
+    wl = Workload("t", B=1, H=2, D=128, grid=(2, 4, 8), n_text=16)
+    q, k, v = make_qkv(wl)
+    assert q.shape == (1, 2, 80, 128)
+    np.testing.assert_array_equal(round_like(q, "bf16"), q)
+    # text tokens carry no position code: their mean is near 0, video's is not
+    assert abs(q[0, 0, 64:].mean()) < 0.1
+
+
+def test_drift_sequence():
+    wl = Workload("t", B=1, H=1, D=64, grid=(1, 8, 8), drift=0.05, plan_reuse=4)
+    seq = make_qkv_sequence(wl, 4)
+    assert len(seq) == 4
+    q0, k0, v0 = seq[0]
+    base = make_qkv(wl)
+    np.testing.assert_array_equal(q0, base[0])
+    d = seq[1][0] - q0
+    assert 0.02 < d.std() < 0.08
+    np.testing.assert_array_equal(seq[3][2], v0)
+
+
+TINY_DIGEST = "aad07a999b1474c410aae359c3bb962103daffb1660dbf0111653148a6aa574a"
