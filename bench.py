@@ -1,0 +1,276 @@
+"""Benchmark of the AB-Attention hot path on one MI355X.
+
+One step = abatt_plan (IBCS selector + SIP sampler) followed by abatt_attend
+(gathered sparse attention) over one synthetic layer, inputs already resident
+in HBM.  Default workload: the Wan2.1-14B 720p layer shape (B=1, 40 heads,
+75600 tokens = 21x45x80 latent grid, D=128, bf16) at a 10% block budget.
+
+Printed: one JSON line with the step throughput as dense-equivalent TFLOP/s
+(4*B*H*N^2*D per step / step time), the per-call times of attend, plan,
+attend + plan/4 (one plan every four denoising steps) and the library's own
+dense kernel, the roofline of the attention kernel (HIP events around each
+abatt_attend launch on the stream it runs on), and the CPU oracle timed on a
+bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload wan14b_720p] [--budget 0.10]
+    python bench.py --probe copy     # plain device copy, for counter calibration
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import CONFIGS, Generator, Workload  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0         # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+PAIR_FLOP = lambda D: 4 * 128 * 4 * D   # one (query block, key block) pair: QK^T + PV
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def make_inputs(wl: Workload, torch, heads=None):
+    """q, k, v bf16 [B,H,N,D] on the GPU, generated head by head on the host."""
+    H = wl.H if heads is None else heads
+    shape = (wl.B, H, wl.N, wl.D)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    q = torch.empty(shape, dtype=dt, device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty_like(q)
+    gen = Generator(wl)
+    for b, h, qh, kh, vh in gen.iter_heads():
+        if h >= H:
+            break
+        q[b, h].copy_(torch.from_numpy(qh).to(dt))
+        k[b, h].copy_(torch.from_numpy(kh).to(dt))
+        v[b, h].copy_(torch.from_numpy(vh).to(dt))
+    return q, k, v
+
+
+def src_sha(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def cpu_baseline(wl: Workload, budget: float, dense_flop_per_head: float):
+    """The oracle (NumPy fp64) on one head of the workload: plan + attend."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    from workloads import make_qkv
+    q, k, v = make_qkv(wl, heads=1)
+    op = oracle.Problem(B=1, H=1, N=wl.N, D=wl.D, n_clusters=wl.n_clusters,
+                        kmeans_iters=wl.kmeans_iters, n_forced_tail=wl.n_text)
+    rows = list(range(op.R))
+    t0 = time.perf_counter()
+    pl = oracle.plan(q, k, op, budget, wl.plan_seed, rows=rows)
+    t1 = time.perf_counter()
+    oracle.attend(q, k, v, pl, op, rows=rows)
+    t2 = time.perf_counter()
+    sec = t2 - t0
+    return {
+        "value": dense_flop_per_head / sec / 1e12,
+        "unit": "TFLOP/s (dense-equivalent)",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"1 of {wl.H} heads ({op.R} plan rows) of {wl.name}: oracle.plan + "
+                  f"oracle.attend at budget {budget}; plan {t1 - t0:.1f} s, attend "
+                  f"{t2 - t1:.1f} s (per-head rate; heads are independent)",
+        "ms_per_call_extrapolated": sec * wl.H * wl.B * 1e3,
+    }
+
+
+def probe_copy(torch, steps: int):
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n, "ms": ms,
+                      "GB/s": 2 * n / ms / 1e6}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan14b_720p", choices=sorted(CONFIGS))
+    ap.add_argument("--budget", type=float, default=None)
+    ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--probe", choices=["copy"], default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the method shards by (batch, head) with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_09_amd as ab
+
+    if args.probe == "copy":
+        probe_copy(torch, args.steps)
+        return
+
+    wl = CONFIGS[args.workload]
+    budget = args.budget if args.budget is not None else \
+        (0.10 if 0.10 in wl.budgets else wl.budgets[0])
+    if budget >= 1.0:
+        raise SystemExit("use a budget below 1 for the sparse path")
+    log(f"workload {wl.name}: B={wl.B} H={wl.H} N={wl.N} D={wl.D} budget={budget}")
+    t0 = time.time()
+    q, k, v = make_inputs(wl, torch)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+
+    prob = ab.Problem(wl.B, wl.H, wl.N, wl.D, n_clusters=wl.n_clusters,
+                      kmeans_iters=wl.kmeans_iters, n_forced_tail=wl.n_text, dtype=wl.dtype)
+    ws = ab.workspace(prob, q.device)
+    pl = ab.empty_plan(prob, ab.nnz_bound(prob, budget), q.device)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        ab.plan(q, k, budget, seed=wl.plan_seed + i, problem=prob, ws=ws, out=pl)
+        if ev is not None:
+            ev[0].record(stream)
+        ab.attend(q, k, v, pl, problem=prob, out=o)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    assert pl.ok(), "plan exceeded its capacity"
+    log("warm-up done")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nnz_list = []
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(end) / args.steps
+    attend_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nnz = pl.nnz()      # plan of the last timed step (every step's nnz is within ~0.1% of it)
+    log(f"timed {args.steps} steps: {step_ms:.3f} ms/step, attend {attend_ms:.3f} ms")
+
+    # plan alone (same workspace), for the per-call split
+    s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s2.record(stream)
+    for i in range(args.steps):
+        ab.plan(q, k, budget, seed=wl.plan_seed + i, problem=prob, ws=ws, out=pl)
+    e2.record(stream)
+    torch.cuda.synchronize()
+    plan_ms = s2.elapsed_time(e2) / args.steps
+
+    dense_ms = None
+    if not args.no_dense:
+        od = torch.empty_like(q)
+        ab.dense(q, k, v, problem=prob, out=od)
+        torch.cuda.synchronize()
+        s3, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s3.record(stream)
+        for _ in range(args.dense_reps):
+            ab.dense(q, k, v, problem=prob, out=od)
+        e3.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = s3.elapsed_time(e3) / args.dense_reps
+        del od
+        log(f"dense {dense_ms:.3f} ms")
+
+    B, H, N, D = wl.B, wl.H, wl.N, wl.D
+    dense_flop = 4.0 * B * H * N * N * D
+    attend_flop = PAIR_FLOP(D) * nnz
+    achieved = attend_flop / (attend_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        t = json.load(open(TRAFFIC_FILE))
+        if t.get("attend_src_sha") == src_sha(os.path.join(
+                ROOT, "block_sparse_attention_09_amd", "csrc", "attend.hip")) \
+                and t.get("workload") == wl.name and abs(t.get("budget", -1) - budget) < 1e-9:
+            traffic = t.get("bytes_per_launch")
+
+    out = {
+        "metric": "sparse attn ms/call + dense-equiv TFLOP/s, Wan2.1-14B shape, ~10% density",
+        "value": dense_flop / (step_ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s (dense-equivalent, plan + attend per step)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded video-grid q/k/v; no model weights)",
+        "config": {
+            "workload": f"{wl.name}: B={B} H={H} N={N} ({'x'.join(map(str, wl.grid))}"
+                        f"{' + %d text' % wl.n_text if wl.n_text else ''}) D={D} {wl.dtype}, "
+                        f"budget {budget}, {wl.n_clusters} clusters, q block 128, kv block 4",
+            "budget": budget,
+            "plan_rows": prob.R,
+            "nnz": nnz,
+            "density": nnz / (prob.R * prob.n_kb),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "k_attend_bf16<128,gather>" if wl.dtype == "bf16" else "k_attend_f32",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+        },
+        "detail": {
+            "attend_ms": attend_ms,
+            "plan_ms": plan_ms,
+            "attend_plus_plan_over_4_ms": attend_ms + plan_ms / 4,
+            "dense_ms": dense_ms,
+            "attend_dense_equiv_tflops": dense_flop / (attend_ms * 1e-3) / 1e12,
+            "speedup_attend_vs_dense": (dense_ms / attend_ms) if dense_ms else None,
+            "speedup_step_vs_dense": (dense_ms / step_ms) if dense_ms else None,
+            "speedup_amortized_vs_dense": (dense_ms / (attend_ms + plan_ms / 4)) if dense_ms else None,
+            "dense_mfma_frac": (dense_flop / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if dense_ms else None,
+            "attend_flop_per_launch": attend_flop,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle on a one-head sample ...")
+        out["cpu_baseline"] = cpu_baseline(wl, budget, 4.0 * N * N * D)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,252 @@
+// C ABI of libabatt: argument checks, workspace layout, kernel launches.
+// Every check runs on the host before any HIP call, so invalid arguments come
+// back as a status code with nothing enqueued (and without a GPU present).
+#include "../../include/abatt.h"
+
+#include <cmath>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+using abatt::Shape;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Validates *p; fills *s.  Returns ABATT_OK, ABATT_EINVAL or ABATT_EUNSUPPORTED.
+abatt_status make_shape(const abatt_problem_t* p, Shape* s) {
+  if (p == nullptr) return ABATT_EINVAL;
+  if (p->B <= 0 || p->H <= 0 || p->N <= 0 || p->D <= 0) return ABATT_EINVAL;
+  if (p->q_block <= 0 || p->kv_block <= 0 || p->n_clusters <= 0 || p->kmeans_iters <= 0)
+    return ABATT_EINVAL;
+  if (p->n_forced_tail < 0 || p->n_forced_tail >= p->N) return ABATT_EINVAL;
+  if (p->n_forced_tail % p->kv_block != 0) return ABATT_EINVAL;
+  if ((p->N - p->n_forced_tail) % p->kv_block != 0) return ABATT_EINVAL;
+  if (!(p->scale > 0.0f) || !std::isfinite(p->scale)) return ABATT_EINVAL;
+  if (p->dtype != ABATT_F32 && p->dtype != ABATT_BF16) return ABATT_EINVAL;
+  if (p->n_clusters > p->q_block) return ABATT_EINVAL;
+  // what the kernels implement
+  if (p->D != 64 && p->D != 128) return ABATT_EUNSUPPORTED;
+  if (p->q_block != 128 || p->kv_block != 4) return ABATT_EUNSUPPORTED;
+  if (p->n_clusters != 8 && p->n_clusters != 16) return ABATT_EUNSUPPORTED;
+  const int64_t n_qb = (p->N + p->q_block - 1) / p->q_block;
+  const int64_t R = (int64_t)p->B * p->H * n_qb;
+  if (R > INT32_MAX / 2) return ABATT_EUNSUPPORTED;
+  s->B = p->B;
+  s->H = p->H;
+  s->N = p->N;
+  s->D = p->D;
+  s->q_block = p->q_block;
+  s->kv_block = p->kv_block;
+  s->n_clusters = p->n_clusters;
+  s->kmeans_iters = p->kmeans_iters;
+  s->n_qb = (int)n_qb;
+  s->n_kbs = (p->N - p->n_forced_tail) / p->kv_block;
+  s->n_kb = s->n_kbs + p->n_forced_tail / p->kv_block;
+  s->R = (int)R;
+  s->scale = p->scale;
+  s->bf16 = p->dtype == ABATT_BF16;
+  return ABATT_OK;
+}
+
+// Dense attention accepts any N (keys past N are masked); the other checks
+// are the same as for the plan problem.
+abatt_status make_dense_shape(const abatt_problem_t* p, Shape* s) {
+  if (p == nullptr) return ABATT_EINVAL;
+  abatt_problem_t q = *p;
+  q.n_forced_tail = 0;
+  const int N = q.N;
+  if (N > 0 && N % 4 != 0) q.N = N + (4 - N % 4);  // only for the block checks
+  abatt_status st = make_shape(&q, s);
+  if (st != ABATT_OK) return st;
+  s->N = N;
+  s->n_qb = (N + s->q_block - 1) / s->q_block;
+  s->R = s->B * s->H * s->n_qb;
+  return ABATT_OK;
+}
+
+struct PlanWs {
+  size_t kmean, mu, w, S, counts, total;
+};
+
+PlanWs plan_ws_layout(const Shape& s) {
+  PlanWs l;
+  size_t off = 0;
+  l.kmean = off;
+  off = align_up(off + (size_t)s.B * s.H * s.n_kbs * s.D * sizeof(float));
+  l.mu = off;
+  off = align_up(off + (size_t)s.R * s.n_clusters * s.D * sizeof(float));
+  l.w = off;
+  off = align_up(off + (size_t)s.R * s.n_clusters * sizeof(float));
+  l.S = off;
+  off = align_up(off + (size_t)s.R * s.n_kbs * sizeof(float));
+  l.counts = off;
+  off = align_up(off + (size_t)s.R * sizeof(int32_t));
+  l.total = off;
+  return l;
+}
+
+size_t sampler_ws_bytes(const Shape& s) { return align_up((size_t)s.R * sizeof(int32_t)); }
+
+abatt_status hip_status(hipError_t e) { return e == hipSuccess ? ABATT_OK : ABATT_EHIP; }
+
+bool budget_ok(double budget) { return budget > 0.0 && budget <= 1.0 && std::isfinite(budget); }
+
+abatt_status check_plan(const Shape& s, const abatt_plan_t* plan, bool need_status) {
+  if (plan == nullptr || plan->row_ptr == nullptr || plan->col_idx == nullptr ||
+      plan->logw == nullptr)
+    return ABATT_EINVAL;
+  if (need_status && plan->status == nullptr) return ABATT_EINVAL;
+  if (plan->capacity < 0) return ABATT_EINVAL;
+  return ABATT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t abatt_plan_rows(const abatt_problem_t* p) {
+  Shape s;
+  return make_shape(p, &s) == ABATT_OK ? (int64_t)s.R : -1;
+}
+
+int64_t abatt_plan_max_nnz(const abatt_problem_t* p) {
+  Shape s;
+  if (make_shape(p, &s) != ABATT_OK) return -1;
+  return (int64_t)s.R * s.n_kb;
+}
+
+int64_t abatt_plan_nnz_bound(const abatt_problem_t* p, double budget) {
+  Shape s;
+  if (make_shape(p, &s) != ABATT_OK || !budget_ok(budget)) return -1;
+  const double m = budget * (double)s.n_kbs;
+  double per = std::ceil(m + 10.0 * std::sqrt(m) + 16.0);
+  if (per > (double)s.n_kbs) per = (double)s.n_kbs;
+  return (int64_t)s.R * ((int64_t)per + (s.n_kb - s.n_kbs));
+}
+
+size_t abatt_plan_workspace_bytes(const abatt_problem_t* p) {
+  Shape s;
+  if (make_shape(p, &s) != ABATT_OK) return 0;
+  return plan_ws_layout(s).total;
+}
+
+size_t abatt_sampler_workspace_bytes(const abatt_problem_t* p) {
+  Shape s;
+  if (make_shape(p, &s) != ABATT_OK) return 0;
+  return sampler_ws_bytes(s);
+}
+
+abatt_status abatt_key_means(const abatt_problem_t* p, const void* K, float* kmean,
+                             hipStream_t stream) {
+  Shape s;
+  abatt_status st = make_shape(p, &s);
+  if (st != ABATT_OK) return st;
+  if (K == nullptr || kmean == nullptr) return ABATT_EINVAL;
+  return hip_status(abatt::launch_key_means(s, K, kmean, stream));
+}
+
+abatt_status abatt_scores(const abatt_problem_t* p, const void* Q, const void* K, float* S,
+                          float* centroids, float* weights, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  abatt_status st = make_shape(p, &s);
+  if (st != ABATT_OK) return st;
+  if (Q == nullptr || K == nullptr || S == nullptr || workspace == nullptr) return ABATT_EINVAL;
+  const PlanWs l = plan_ws_layout(s);
+  if (workspace_bytes < l.total) return ABATT_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  float* kmean = reinterpret_cast<float*>(ws + l.kmean);
+  float* mu = centroids ? centroids : reinterpret_cast<float*>(ws + l.mu);
+  float* w = weights ? weights : reinterpret_cast<float*>(ws + l.w);
+  hipError_t e = abatt::launch_key_means(s, K, kmean, stream);
+  if (e == hipSuccess) e = abatt::launch_kmeans(s, Q, mu, w, stream);
+  if (e == hipSuccess) e = abatt::launch_scores(s, mu, w, kmean, S, stream);
+  return hip_status(e);
+}
+
+abatt_status abatt_plan_from_scores(const abatt_problem_t* p, const float* S, double budget,
+                                    uint64_t seed, void* workspace, size_t workspace_bytes,
+                                    abatt_plan_t* plan, hipStream_t stream) {
+  Shape s;
+  abatt_status st = make_shape(p, &s);
+  if (st != ABATT_OK) return st;
+  if (S == nullptr || workspace == nullptr || !budget_ok(budget)) return ABATT_EINVAL;
+  st = check_plan(s, plan, true);
+  if (st != ABATT_OK) return st;
+  if (workspace_bytes < sampler_ws_bytes(s)) return ABATT_EWORKSPACE;
+  if (plan->capacity < (int64_t)s.R * (s.n_kb - s.n_kbs)) return ABATT_ECAPACITY;
+  int32_t* counts = static_cast<int32_t*>(workspace);
+  return hip_status(abatt::launch_sampler(s, S, budget, seed, counts, plan->row_ptr,
+                                          plan->col_idx, plan->logw, plan->capacity,
+                                          plan->status, stream));
+}
+
+abatt_status abatt_plan(const abatt_problem_t* p, const void* Q, const void* K, double budget,
+                        uint64_t seed, void* workspace, size_t workspace_bytes,
+                        abatt_plan_t* plan, hipStream_t stream) {
+  Shape s;
+  abatt_status st = make_shape(p, &s);
+  if (st != ABATT_OK) return st;
+  if (Q == nullptr || K == nullptr || workspace == nullptr || !budget_ok(budget))
+    return ABATT_EINVAL;
+  st = check_plan(s, plan, true);
+  if (st != ABATT_OK) return st;
+  const PlanWs l = plan_ws_layout(s);
+  if (workspace_bytes < l.total) return ABATT_EWORKSPACE;
+  if (plan->capacity < (int64_t)s.R * (s.n_kb - s.n_kbs)) return ABATT_ECAPACITY;
+  char* ws = static_cast<char*>(workspace);
+  float* kmean = reinterpret_cast<float*>(ws + l.kmean);
+  float* mu = reinterpret_cast<float*>(ws + l.mu);
+  float* w = reinterpret_cast<float*>(ws + l.w);
+  float* S = reinterpret_cast<float*>(ws + l.S);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + l.counts);
+  hipError_t e = abatt::launch_key_means(s, K, kmean, stream);
+  if (e == hipSuccess) e = abatt::launch_kmeans(s, Q, mu, w, stream);
+  if (e == hipSuccess) e = abatt::launch_scores(s, mu, w, kmean, S, stream);
+  if (e == hipSuccess)
+    e = abatt::launch_sampler(s, S, budget, seed, counts, plan->row_ptr, plan->col_idx,
+                              plan->logw, plan->capacity, plan->status, stream);
+  return hip_status(e);
+}
+
+abatt_status abatt_attend(const abatt_problem_t* p, const void* Q, const void* K, const void* V,
+                          const abatt_plan_t* plan, void* O, float* lse, hipStream_t stream) {
+  Shape s;
+  abatt_status st = make_shape(p, &s);
+  if (st != ABATT_OK) return st;
+  if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr) return ABATT_EINVAL;
+  st = check_plan(s, plan, false);
+  if (st != ABATT_OK) return st;
+  return hip_status(abatt::launch_attend(s, Q, K, V, plan->row_ptr, plan->col_idx, plan->logw,
+                                         plan->capacity, plan->status, O, lse, true, stream));
+}
+
+abatt_status abatt_dense(const abatt_problem_t* p, const void* Q, const void* K, const void* V,
+                         void* O, float* lse, hipStream_t stream) {
+  Shape s;
+  abatt_status st = make_dense_shape(p, &s);
+  if (st != ABATT_OK) return st;
+  if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr) return ABATT_EINVAL;
+  return hip_status(abatt::launch_attend(s, Q, K, V, nullptr, nullptr, nullptr, 0, nullptr, O,
+                                         lse, false, stream));
+}
+
+const char* abatt_status_str(abatt_status s) {
+  switch (s) {
+    case ABATT_OK: return "ok";
+    case ABATT_EINVAL: return "invalid argument";
+    case ABATT_EUNSUPPORTED: return "unsupported problem (D, block sizes or cluster count)";
+    case ABATT_EWORKSPACE: return "workspace too small";
+    case ABATT_ECAPACITY: return "plan capacity too small";
+    case ABATT_EHIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* abatt_version(void) { return "abatt 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,412 @@
+// Gathered-KV flash attention with the Horvitz-Thompson logit shift, and the
+// dense path built from the same tile core.
+//
+// [hamidun] = news.hamidun.com, "AB-Attention speeds up video generation by up
+// to 2.23x and skips 92% of attention", section "AB-Attention's three
+// techniques": SIP keeps ordinary softmax attention and adds log(1/pi) to the
+// logits of a kept block; the third technique gathers the kept 4-token K/V
+// blocks by index into full compute tiles without permuting tokens
+// ([zerohour] = zerohour.day, "AB-Attention approximates dense video attention
+// at high sparsity", key facts, says the same of the kernel).
+//
+// bf16 kernel (gfx950), one work-group of 4 waves per plan row (128 queries):
+//   * wave w owns queries 32w..32w+31; its Q slice stays in registers as the
+//     B operand of S^T = K Q^T (bf16 MFMA 32x32x16, fp32 accumulation), so a
+//     lane ends up holding 32 logits of ONE query (lane%32) and the row max
+//     needs a single exchange between the two half-waves;
+//   * keys arrive in chunks of 16 kept blocks = 64 keys.  Each 4-token block
+//     of a head is 4*D*2 contiguous bytes, so one wave-wide 16-byte load
+//     gathers a whole block (D=128) into the K tile.  V is written to LDS
+//     transposed and converted to fp16 (exact for bf16 values in fp16's
+//     normal range) so that PV can run as O^T = V^T P^T on fp16 MFMA with
+//     the probabilities straight from the softmax registers: the key order
+//     inside an MFMA k-step is chosen to match what each lane already holds;
+//   * two LDS buffers, global loads for chunk c+1 issued before chunk c is
+//     computed, one barrier per chunk;
+//   * online softmax in the exp2 domain; the running max is only moved when
+//     a chunk raises it by more than 8 (log2 units), so most chunks skip the
+//     rescale of the accumulators (p then stays below 2^8, fine for fp16);
+//   * work-groups are remapped so consecutive query blocks of a head share an
+//     XCD (and its L2), which is where gathered K/V blocks get reused.
+// fp32 kernel: plain fp32 arithmetic (one thread per query), used for fp32
+// problems.
+#include "common.h"
+#include "kernels.h"
+
+namespace abatt {
+
+constexpr float kRescaleLog2 = 8.0f;
+
+template <int D, bool kGather>
+__global__ __launch_bounds__(256, 2) void k_attend_bf16(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ col_idx, const float* __restrict__ logw, int64_t capacity,
+    const int32_t* __restrict__ status, uint16_t* __restrict__ O, float* __restrict__ lse, int N,
+    int n_qb, int n_kb, int R, float scale_log2) {
+  constexpr int KS = D / 16;          // QK^T k-steps
+  constexpr int DT = D / 32;          // PV output tiles
+  constexpr int KROW = D + 8;         // K tile row stride (bf16)
+  constexpr int VROW = 64 + 4;        // V^T tile row stride (fp16)
+  constexpr int SLOTS = 2 * D / 64;   // per-lane load slots per chunk
+  constexpr int HALF = D / 2;         // 16-byte K chunks (and V d-pairs) per block
+  __shared__ __align__(16) uint16_t Ks[2][64 * KROW];
+  __shared__ __align__(16) uint16_t Vt[2][D * VROW];
+  __shared__ __align__(16) float lw2[2][64];
+
+  const int r = xcd_remap(blockIdx.x, R);
+  const int qb = r % n_qb;
+  const int64_t bh = r / n_qb;
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63, l32 = lane & 31, hh = lane >> 5;
+
+  int64_t start = 0;
+  int nblk;
+  if constexpr (kGather) {
+    const int64_t a = row_ptr[r], b = row_ptr[r + 1];
+    const bool bad = (status != nullptr && *status != 0) || a < 0 || b < a || b > capacity;
+    start = a;
+    nblk = bad ? 0 : (int)(b - a);
+  } else {
+    nblk = (N + 3) / 4;
+  }
+  const int nchunk = (nblk + 15) / 16;
+
+  const uint16_t* Kh = K + bh * N * D;
+  const uint16_t* Vh = V + bh * N * D;
+
+  const int qrow = qb * 128 + 32 * wv + l32;
+  bf16x8 qreg[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (qrow < N)
+      qreg[s] = *reinterpret_cast<const bf16x8*>(Q + (bh * N + qrow) * D + 16 * s + 8 * hh);
+    else
+      qreg[s] = bf16x8{};
+  }
+
+  // block id of block bi (0..15) of chunk c; lw gets its log2-domain shift
+  auto block_of = [&](int c, int bi, float& lw) -> int {
+    const int idx = c * 16 + bi;
+    if constexpr (kGather) {
+      if (idx < nblk) {
+        const int id = col_idx[start + idx];
+        if (id >= 0 && id < n_kb) {
+          lw = logw[start + idx] * kLog2e;
+          return id;
+        }
+      }
+      lw = -INFINITY;
+      return 0;
+    } else {
+      lw = 0.f;
+      return idx;
+    }
+  };
+  auto token = [&](int id, int k) -> int64_t {
+    const int tok = 4 * id + k;
+    if constexpr (kGather) return tok;
+    return tok < N ? tok : N - 1;
+  };
+
+  u32x4 kpre[SLOTS];
+  uint32_t vpre[SLOTS][4];
+  float lwpre = 0.f;
+
+  auto load_chunk = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      const int lin = i * 64 + lane;
+      const int bi = 4 * wv + lin / HALF;
+      const int rem = lin % HALF;
+      float lw;
+      const int id = block_of(c, bi, lw);
+      const int key = rem / (D / 8), dc = rem % (D / 8);
+      kpre[i] = *reinterpret_cast<const u32x4*>(Kh + token(id, key) * D + 8 * dc);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        vpre[i][k] = *reinterpret_cast<const uint32_t*>(Vh + token(id, k) * D + 2 * rem);
+    }
+    if (t < 64) {
+      float lw;
+      const int id = block_of(c, t >> 2, lw);
+      if constexpr (!kGather) lw = (4 * id + (t & 3) < N) ? 0.f : -INFINITY;
+      lwpre = lw;
+    }
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      const int lin = i * 64 + lane;
+      const int bi = 4 * wv + lin / HALF;
+      const int rem = lin % HALF;
+      const int key = rem / (D / 8), dc = rem % (D / 8);
+      *reinterpret_cast<u32x4*>(&Ks[buf][(4 * bi + key) * KROW + 8 * dc]) = kpre[i];
+      // V^T: rows 2*rem (even dim) and 2*rem+1 (odd dim), columns 4*bi..4*bi+3
+      const uint32_t* v = vpre[i];
+      const u32x2 ev = {pack_f16_rtz(__uint_as_float(v[0] << 16), __uint_as_float(v[1] << 16)),
+                        pack_f16_rtz(__uint_as_float(v[2] << 16), __uint_as_float(v[3] << 16))};
+      const u32x2 od = {pack_f16_rtz(__uint_as_float(v[0] & 0xffff0000u),
+                                     __uint_as_float(v[1] & 0xffff0000u)),
+                        pack_f16_rtz(__uint_as_float(v[2] & 0xffff0000u),
+                                     __uint_as_float(v[3] & 0xffff0000u))};
+      *reinterpret_cast<u32x2*>(&Vt[buf][(2 * rem) * VROW + 4 * bi]) = ev;
+      *reinterpret_cast<u32x2*>(&Vt[buf][(2 * rem + 1) * VROW + 4 * bi]) = od;
+    }
+    if (t < 64) lw2[buf][t] = lwpre;
+  };
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int u = 0; u < DT; ++u) oacc[u] = f32x16{};
+  float m_used = -INFINITY, lsum = 0.f;
+
+  if (nchunk > 0) {
+    load_chunk(0);
+    store_chunk(0);
+  }
+  __syncthreads();
+
+  for (int c = 0; c < nchunk; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nchunk) load_chunk(c + 1);
+
+    // S^T tile: lane holds query l32, keys 32*tt + 8*(v/4) + 4*hh + v%4
+    f32x16 sacc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sacc[tt] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(&Ks[buf][(32 * tt + l32) * KROW + 16 * s + 8 * hh]);
+        sacc[tt] = mfma_bf16_32x32x16(a, qreg[s], sacc[tt]);
+      }
+    }
+    float x[32];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 sh = *reinterpret_cast<const f32x4*>(&lw2[buf][32 * tt + 8 * g + 4 * hh]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float z = fmaf(sacc[tt][4 * g + q], scale_log2, sh[q]);
+          x[16 * tt + 4 * g + q] = z;
+          mloc = fmaxf(mloc, z);
+        }
+      }
+    }
+    const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const bool need = mrow > m_used + kRescaleLog2;
+    if (__any(need)) {
+      const float alpha = need ? exp2f(m_used - mrow) : 1.f;
+      if (need) m_used = mrow;
+      lsum *= alpha;
+#pragma unroll
+      for (int u = 0; u < DT; ++u) oacc[u] *= alpha;
+    }
+    const float mref = m_used == -INFINITY ? 0.f : m_used;
+    uint32_t pk[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p0 = exp2f(x[2 * i] - mref), p1 = exp2f(x[2 * i + 1] - mref);
+      lsum += p0 + p1;
+      pk[i] = pack_f16_rne(p0, p1);
+    }
+    // O^T += V^T P^T; k-step (tt, gp) covers keys 32tt+16gp .. +15 in the
+    // order lane-half hh holds them: 4hh+{0..3}, 8+4hh+{0..3}
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp) {
+        const int pb = 8 * tt + 4 * gp;
+        const f16x8 pop =
+            __builtin_bit_cast(f16x8, u32x4{pk[pb], pk[pb + 1], pk[pb + 2], pk[pb + 3]});
+#pragma unroll
+        for (int u = 0; u < DT; ++u) {
+          const uint16_t* row = &Vt[buf][(32 * u + l32) * VROW + 32 * tt + 16 * gp + 4 * hh];
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 8);
+          const f16x8 vop = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          oacc[u] = mfma_f16_32x32x16(vop, pop, oacc[u]);
+        }
+      }
+    }
+    if (c + 1 < nchunk) store_chunk(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: O^T lane layout = query l32, dims 32u + 8g + 4hh + (0..3)
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  if (qrow < N) {
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    uint16_t* orow = O + (bh * N + qrow) * D;
+#pragma unroll
+    for (int u = 0; u < DT; ++u) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t b0 = f32_to_bf16_bits(oacc[u][4 * g] * inv);
+        const uint32_t b1 = f32_to_bf16_bits(oacc[u][4 * g + 1] * inv);
+        const uint32_t b2 = f32_to_bf16_bits(oacc[u][4 * g + 2] * inv);
+        const uint32_t b3 = f32_to_bf16_bits(oacc[u][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + 32 * u + 8 * g + 4 * hh) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+      }
+    }
+    if (hh == 0 && lse != nullptr)
+      lse[bh * N + qrow] = ltot > 0.f ? (m_used + log2f(ltot)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: one thread per query, 32-key chunks staged in LDS.
+// ---------------------------------------------------------------------------
+template <int D, bool kGather>
+__global__ __launch_bounds__(128) void k_attend_f32(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    const float* __restrict__ logw, int64_t capacity, const int32_t* __restrict__ status,
+    float* __restrict__ O, float* __restrict__ lse, int N, int n_qb, int n_kb, int R,
+    float scale_log2) {
+  constexpr int CK = 32;  // keys per chunk = 8 blocks
+  __shared__ __align__(16) float Kf[CK * D];
+  __shared__ __align__(16) float Vf[CK * D];
+  __shared__ float lwk[CK];
+
+  const int r = xcd_remap(blockIdx.x, R);
+  const int qb = r % n_qb;
+  const int64_t bh = r / n_qb;
+  const int t = threadIdx.x;
+  const int qrow = qb * 128 + t;
+
+  int64_t start = 0;
+  int nblk;
+  if constexpr (kGather) {
+    const int64_t a = row_ptr[r], b = row_ptr[r + 1];
+    const bool bad = (status != nullptr && *status != 0) || a < 0 || b < a || b > capacity;
+    start = a;
+    nblk = bad ? 0 : (int)(b - a);
+  } else {
+    nblk = (N + 3) / 4;
+  }
+  const int nchunk = (nblk + 7) / 8;
+  const float* Kh = K + bh * N * D;
+  const float* Vh = V + bh * N * D;
+
+  float q[D], o[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    q[e] = qrow < N ? Q[(bh * N + qrow) * D + e] : 0.f;
+    o[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+
+  for (int c = 0; c < nchunk; ++c) {
+    __syncthreads();
+    for (int i = t; i < CK * D / 4; i += 128) {
+      const int key = (4 * i) / D, e = (4 * i) % D;
+      const int idx = c * 8 + key / 4;
+      int id = 0;
+      float lw = -INFINITY;
+      if constexpr (kGather) {
+        if (idx < nblk) {
+          const int cid = col_idx[start + idx];
+          if (cid >= 0 && cid < n_kb) {
+            id = cid;
+            lw = logw[start + idx] * kLog2e;
+          }
+        }
+      } else {
+        id = idx;
+        lw = (4 * idx + (key & 3) < N) ? 0.f : -INFINITY;
+      }
+      int64_t tok = 4 * (int64_t)id + (key & 3);
+      if (tok >= N) tok = N - 1;
+      *reinterpret_cast<f32x4*>(&Kf[key * D + e]) = *reinterpret_cast<const f32x4*>(Kh + tok * D + e);
+      *reinterpret_cast<f32x4*>(&Vf[key * D + e]) = *reinterpret_cast<const f32x4*>(Vh + tok * D + e);
+      if (e == 0) lwk[key] = lw;
+    }
+    __syncthreads();
+    float z[CK];
+    float cm = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < CK; ++k) {
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; e += 4) {
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(&Kf[k * D + e]);
+        dot = fmaf(q[e], kv[0], dot);
+        dot = fmaf(q[e + 1], kv[1], dot);
+        dot = fmaf(q[e + 2], kv[2], dot);
+        dot = fmaf(q[e + 3], kv[3], dot);
+      }
+      z[k] = fmaf(dot, scale_log2, lwk[k]);
+      cm = fmaxf(cm, z[k]);
+    }
+    const float mn = fmaxf(m, cm);
+    if (mn == -INFINITY) continue;
+    const float alpha = exp2f(m - mn);
+    m = mn;
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < D; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int k = 0; k < CK; ++k) {
+      const float p = exp2f(z[k] - m);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < D; e += 4) {
+        const f32x4 vv = *reinterpret_cast<const f32x4*>(&Vf[k * D + e]);
+        o[e] = fmaf(p, vv[0], o[e]);
+        o[e + 1] = fmaf(p, vv[1], o[e + 1]);
+        o[e + 2] = fmaf(p, vv[2], o[e + 2]);
+        o[e + 3] = fmaf(p, vv[3], o[e + 3]);
+      }
+    }
+  }
+  if (qrow < N) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* orow = O + (bh * N + qrow) * D;
+#pragma unroll
+    for (int e = 0; e < D; e += 4)
+      *reinterpret_cast<f32x4*>(orow + e) = f32x4{o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv};
+    if (lse != nullptr) lse[bh * N + qrow] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, bool kGather>
+static void launch_attend_t(const Shape& s, const void* Q, const void* K, const void* V,
+                            const int32_t* row_ptr, const int32_t* col_idx, const float* logw,
+                            int64_t capacity, const int32_t* status, void* O, float* lse,
+                            hipStream_t st) {
+  const float sl2 = s.scale * kLog2e;
+  if (s.bf16) {
+    k_attend_bf16<D, kGather><<<s.R, 256, 0, st>>>(
+        (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, row_ptr, col_idx, logw,
+        capacity, status, (uint16_t*)O, lse, s.N, s.n_qb, s.n_kb, s.R, sl2);
+  } else {
+    k_attend_f32<D, kGather><<<s.R, 128, 0, st>>>(
+        (const float*)Q, (const float*)K, (const float*)V, row_ptr, col_idx, logw, capacity,
+        status, (float*)O, lse, s.N, s.n_qb, s.n_kb, s.R, sl2);
+  }
+}
+
+hipError_t launch_attend(const Shape& s, const void* Q, const void* K, const void* V,
+                         const int32_t* row_ptr, const int32_t* col_idx, const float* logw,
+                         int64_t capacity, const int32_t* status, void* O, float* lse,
+                         bool gather, hipStream_t st) {
+  if (s.D == 128) {
+    if (gather)
+      launch_attend_t<128, true>(s, Q, K, V, row_ptr, col_idx, logw, capacity, status, O, lse, st);
+    else
+      launch_attend_t<128, false>(s, Q, K, V, row_ptr, col_idx, logw, capacity, status, O, lse, st);
+  } else {
+    if (gather)
+      launch_attend_t<64, true>(s, Q, K, V, row_ptr, col_idx, logw, capacity, status, O, lse, st);
+    else
+      launch_attend_t<64, false>(s, Q, K, V, row_ptr, col_idx, logw, capacity, status, O, lse, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace abatt

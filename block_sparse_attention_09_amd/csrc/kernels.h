@@ -1,0 +1,43 @@
+// Host-side launchers of the gfx950 kernels (internal to libabatt).
+// Each returns the hipError_t of its launch(es); shapes are checked by the
+// caller (abatt.cpp) before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace abatt {
+
+struct Shape {
+  int B, H, N, D;
+  int q_block, kv_block, n_clusters, kmeans_iters;
+  int n_qb;      // ceil(N / q_block)
+  int n_kbs;     // sparse (scored) key blocks
+  int n_kb;      // all key blocks incl. forced
+  int R;         // B*H*n_qb plan rows
+  float scale;
+  bool bf16;     // dtype of Q/K/V/O
+};
+
+// key_means.hip
+hipError_t launch_key_means(const Shape& s, const void* K, float* kmean, hipStream_t st);
+
+// kmeans.hip: centroids [R, C, D] fp32 and weights [R, C] fp32
+hipError_t launch_kmeans(const Shape& s, const void* Q, float* mu, float* w, hipStream_t st);
+
+// score.hip: S [R, n_kbs] fp32 from centroids, weights and key means
+hipError_t launch_scores(const Shape& s, const float* mu, const float* w, const float* kmean,
+                         float* S, hipStream_t st);
+
+// sampler.hip: counts -> row_ptr -> col_idx/logw
+hipError_t launch_sampler(const Shape& s, const float* S, double budget, uint64_t seed,
+                          int32_t* counts, int32_t* row_ptr, int32_t* col_idx, float* logw,
+                          int64_t capacity, int32_t* status, hipStream_t st);
+
+// attend.hip: gathered (plan != null) or dense attention
+hipError_t launch_attend(const Shape& s, const void* Q, const void* K, const void* V,
+                         const int32_t* row_ptr, const int32_t* col_idx, const float* logw,
+                         int64_t capacity, const int32_t* status, void* O, float* lse,
+                         bool gather, hipStream_t st);
+
+}  // namespace abatt

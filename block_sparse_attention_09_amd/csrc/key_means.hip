@@ -1,0 +1,89 @@
+// Mean key of every sparse 4-token key block.
+//
+// [hamidun] "AB-Attention's three techniques", IBCS paragraph: key blocks are
+// scored through their averaged keys; the third technique fixes the key block
+// at 4 consecutive tokens.  HBM-bound: each block's 4 rows are read once
+// (16-byte lane loads, consecutive lanes on consecutive bytes) and one fp32
+// row is written.
+#include "common.h"
+#include "kernels.h"
+
+namespace abatt {
+
+// bf16 input: one thread = 8 dims of one block (4 x 16-byte loads).
+template <int D>
+__global__ __launch_bounds__(256) void k_key_means_bf16(const uint16_t* __restrict__ K,
+                                                        float* __restrict__ kmean,
+                                                        int64_t total, int N, int n_kbs) {
+  constexpr int CH = D / 8;  // 16-byte chunks per row
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % CH);
+    const int64_t bj = i / CH;  // bh * n_kbs + j
+    const int j = (int)(bj % n_kbs);
+    const int64_t bh = bj / n_kbs;
+    const uint16_t* src = K + (bh * N + 4 * (int64_t)j) * D + 8 * c;
+    u32x4 r0 = *reinterpret_cast<const u32x4*>(src);
+    u32x4 r1 = *reinterpret_cast<const u32x4*>(src + D);
+    u32x4 r2 = *reinterpret_cast<const u32x4*>(src + 2 * D);
+    u32x4 r3 = *reinterpret_cast<const u32x4*>(src + 3 * D);
+    float out[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a0 = bf16_bits_to_f32(r0[e] & 0xffffu), b0 = bf16_bits_to_f32(r0[e] >> 16);
+      const float a1 = bf16_bits_to_f32(r1[e] & 0xffffu), b1 = bf16_bits_to_f32(r1[e] >> 16);
+      const float a2 = bf16_bits_to_f32(r2[e] & 0xffffu), b2 = bf16_bits_to_f32(r2[e] >> 16);
+      const float a3 = bf16_bits_to_f32(r3[e] & 0xffffu), b3 = bf16_bits_to_f32(r3[e] >> 16);
+      out[2 * e] = (((a0 + a1) + a2) + a3) * 0.25f;
+      out[2 * e + 1] = (((b0 + b1) + b2) + b3) * 0.25f;
+    }
+    float* dst = kmean + bj * D + 8 * c;
+    *reinterpret_cast<f32x4*>(dst) = f32x4{out[0], out[1], out[2], out[3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{out[4], out[5], out[6], out[7]};
+  }
+}
+
+// fp32 input: one thread = 4 dims of one block.
+template <int D>
+__global__ __launch_bounds__(256) void k_key_means_f32(const float* __restrict__ K,
+                                                       float* __restrict__ kmean,
+                                                       int64_t total, int N, int n_kbs) {
+  constexpr int CH = D / 4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % CH);
+    const int64_t bj = i / CH;
+    const int j = (int)(bj % n_kbs);
+    const int64_t bh = bj / n_kbs;
+    const float* src = K + (bh * N + 4 * (int64_t)j) * D + 4 * c;
+    f32x4 r0 = *reinterpret_cast<const f32x4*>(src);
+    f32x4 r1 = *reinterpret_cast<const f32x4*>(src + D);
+    f32x4 r2 = *reinterpret_cast<const f32x4*>(src + 2 * D);
+    f32x4 r3 = *reinterpret_cast<const f32x4*>(src + 3 * D);
+    f32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (((r0[e] + r1[e]) + r2[e]) + r3[e]) * 0.25f;
+    *reinterpret_cast<f32x4*>(kmean + bj * D + 4 * c) = o;
+  }
+}
+
+hipError_t launch_key_means(const Shape& s, const void* K, float* kmean, hipStream_t st) {
+  const int64_t blocks = (int64_t)s.B * s.H * s.n_kbs;
+  const int64_t total = blocks * (s.bf16 ? s.D / 8 : s.D / 4);
+  const int64_t want = (total + 255) / 256;
+  const int grid = (int)(want < 65536 ? want : 65536);
+  if (s.bf16) {
+    if (s.D == 128)
+      k_key_means_bf16<128><<<grid, 256, 0, st>>>((const uint16_t*)K, kmean, total, s.N, s.n_kbs);
+    else
+      k_key_means_bf16<64><<<grid, 256, 0, st>>>((const uint16_t*)K, kmean, total, s.N, s.n_kbs);
+  } else {
+    if (s.D == 128)
+      k_key_means_f32<128><<<grid, 256, 0, st>>>((const float*)K, kmean, total, s.N, s.n_kbs);
+    else
+      k_key_means_f32<64><<<grid, 256, 0, st>>>((const float*)K, kmean, total, s.N, s.n_kbs);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace abatt

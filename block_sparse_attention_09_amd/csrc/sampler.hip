@@ -1,0 +1,336 @@
+// SIP sampler: inclusion probabilities, Philox draws, CSR plan.
+//
+// [hamidun] = news.hamidun.com, "AB-Attention speeds up video generation by up
+// to 2.23x and skips 92% of attention", section "AB-Attention's three
+// techniques", SIP paragraph: each key block is sampled with probability
+// proportional to its score, the most important blocks are certain, and a
+// kept block is weighted by the inverse of its probability (Horvitz-Thompson),
+// applied as the logit shift log(1/pi).
+//
+// Per plan row (one work-group, the score row staged in LDS):
+//   * pi: m = budget * n expected blocks; repeat c = (m - #certain) /
+//     sum(uncertain positive scores) and make every uncertain block with
+//     c*s >= 1 certain, until none is added.  The certain set is always a top
+//     set of the scores, so it is held as a threshold theta (certain iff
+//     s >= theta).  float64 throughout; sums are fixed-order tree reductions,
+//     so every run gives the same bits.
+//   * draws: block j uses word j%4 of Philox4x64-10(counter (j/4, qb, h, b),
+//     key (seed, 0)); kept iff its top 53 bits < pi_j * 2^53 (exact compare).
+// k_sip_count writes the row's kept count; k_scan turns counts into row_ptr
+// (and flags a plan that exceeds its capacity); k_sip_fill repeats the same
+// deterministic solve and draws and writes ascending block ids and
+// logw = -ln(pi) (float64 log, rounded to fp32; 0 where pi = 1).  Forced
+// (text) blocks follow the sampled ones with logw 0.
+#include "common.h"
+#include "kernels.h"
+
+namespace abatt {
+
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): 10 rounds of two
+// 64x64->128-bit multiplies with a Weyl-sequence key schedule.
+__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+constexpr int kSampT = 256;
+constexpr int kSampWaves = kSampT / 64;
+constexpr double kTwo53 = 9007199254740992.0;
+
+struct Red {
+  double d[kSampWaves];
+  float f[kSampWaves];
+  int i[kSampWaves];
+};
+
+__device__ __forceinline__ double block_sum_f64(double v, Red& red) {
+  v = wave_sum_f64(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red.d[w] = v;
+  __syncthreads();
+  double s = red.d[0];
+#pragma unroll
+  for (int k = 1; k < kSampWaves; ++k) s += red.d[k];
+  __syncthreads();
+  return s;
+}
+
+__device__ __forceinline__ float block_min_f32(float v, Red& red) {
+  v = wave_min(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red.f[w] = v;
+  __syncthreads();
+  float s = red.f[0];
+#pragma unroll
+  for (int k = 1; k < kSampWaves; ++k) s = fminf(s, red.f[k]);
+  __syncthreads();
+  return s;
+}
+
+__device__ __forceinline__ int block_sum_i32(int v, Red& red) {
+  v = wave_sum_i32(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red.i[w] = v;
+  __syncthreads();
+  int s = red.i[0];
+#pragma unroll
+  for (int k = 1; k < kSampWaves; ++k) s += red.i[k];
+  __syncthreads();
+  return s;
+}
+
+struct PiSolve {
+  int mode;      // 0: every block pi=1; 1: pi=1 on positive scores; 2: capped-proportional
+  double c;      // proportionality constant (mode 2)
+  float theta;   // certain iff s >= theta (mode 2)
+};
+
+__device__ __forceinline__ double pi_of(float s, const PiSolve& ps) {
+  if (ps.mode == 0) return 1.0;
+  if (!(s > 0.f)) return 0.0;
+  if (ps.mode == 1 || s >= ps.theta) return 1.0;
+  return ps.c * (double)s;
+}
+
+__device__ PiSolve solve_pi(const float* s, int n, double budget, Red& red) {
+  PiSolve ps;
+  ps.c = 0.0;
+  ps.theta = INFINITY;
+  const double m = budget * (double)n;
+  if (m >= (double)n) {
+    ps.mode = 0;
+    return ps;
+  }
+  int npos = 0;
+  for (int j = threadIdx.x; j < n; j += kSampT) npos += s[j] > 0.f;
+  npos = block_sum_i32(npos, red);
+  if (m >= (double)npos) {
+    ps.mode = 1;
+    return ps;
+  }
+  ps.mode = 2;
+  int ncert = 0;
+  float theta = INFINITY;
+  for (;;) {
+    double part = 0.0;
+    for (int j = threadIdx.x; j < n; j += kSampT) {
+      const float v = s[j];
+      if (v > 0.f && v < theta) part += (double)v;
+    }
+    const double sum = block_sum_f64(part, red);
+    if (!(sum > 0.0)) break;
+    const double c = (m - (double)ncert) / sum;
+    ps.c = c;
+    float cand = INFINITY;
+    for (int j = threadIdx.x; j < n; j += kSampT) {
+      const float v = s[j];
+      if (v > 0.f && v < theta && c * (double)v >= 1.0) cand = fminf(cand, v);
+    }
+    cand = block_min_f32(cand, red);
+    if (cand == INFINITY) break;
+    theta = cand;
+    ps.theta = theta;
+    int k = 0;
+    for (int j = threadIdx.x; j < n; j += kSampT) k += s[j] >= theta;
+    ncert = block_sum_i32(k, red);
+  }
+  return ps;
+}
+
+// Stage the row in LDS (or read it from global memory when it does not fit).
+template <bool kLds>
+__device__ __forceinline__ const float* stage_row(const float* g, int n, float* lds) {
+  if constexpr (kLds) {
+    for (int j = threadIdx.x; j < n; j += kSampT) lds[j] = g[j];
+    __syncthreads();
+    return lds;
+  } else {
+    return g;
+  }
+}
+
+// Kept-bit mask (4 bits) of the four blocks of Philox group g.
+__device__ __forceinline__ uint32_t draw_group(const float* s, int n, int g, int qb, int h, int b,
+                                               uint64_t seed, const PiSolve& ps) {
+  uint64_t c[4] = {(uint64_t)g, (uint64_t)qb, (uint64_t)h, (uint64_t)b};
+  philox4x64_10(c, seed, 0ull);
+  uint32_t mask = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = 4 * g + i;
+    if (j < n) {
+      const double pi = pi_of(s[j], ps);
+      const double u = (double)(c[i] >> 11);
+      if (u < pi * kTwo53) mask |= 1u << i;
+    }
+  }
+  return mask;
+}
+
+template <bool kLds>
+__global__ __launch_bounds__(kSampT) void k_sip_count(const float* __restrict__ S, int n,
+                                                     int n_forced, int n_qb, int H,
+                                                     double budget, uint64_t seed,
+                                                     int32_t* __restrict__ counts) {
+  extern __shared__ __align__(16) float srow[];
+  __shared__ Red red;
+  const int r = blockIdx.x;
+  const int qb = r % n_qb, bh = r / n_qb, h = bh % H, b = bh / H;
+  const float* s = stage_row<kLds>(S + (int64_t)r * n, n, srow);
+  const PiSolve ps = solve_pi(s, n, budget, red);
+  const int groups = (n + 3) / 4;
+  int cnt = 0;
+  for (int g = threadIdx.x; g < groups; g += kSampT)
+    cnt += __popc(draw_group(s, n, g, qb, h, b, seed, ps));
+  cnt = block_sum_i32(cnt, red);
+  if (threadIdx.x == 0) counts[r] = cnt + n_forced;
+}
+
+// Exclusive scan of the row counts -> row_ptr (single work-group).
+__global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ counts, int R,
+                                               int32_t* __restrict__ row_ptr, int64_t capacity,
+                                               int32_t* __restrict__ status) {
+  __shared__ int64_t wsum[16];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int per = (R + 1023) / 1024;
+  const int lo = min(t * per, R), hi = min(lo + per, R);
+  int64_t local = 0;
+  for (int i = lo; i < hi; ++i) local += counts[i];
+  // inclusive scan within the wave
+  int64_t incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t up = __shfl_up(incl, o);
+    if (lane >= o) incl += up;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int64_t before = 0, total = 0;
+  for (int k = 0; k < 16; ++k) {
+    if (k < w) before += wsum[k];
+    total += wsum[k];
+  }
+  int64_t run = before + incl - local;
+  const int64_t cap32 = 0x7fffffff;
+  for (int i = lo; i < hi; ++i) {
+    row_ptr[i] = (int32_t)(run < cap32 ? run : cap32);
+    run += counts[i];
+  }
+  if (t == 0) {
+    row_ptr[R] = (int32_t)(total < cap32 ? total : cap32);
+    *status = (total > capacity || total > cap32) ? 1 : 0;
+  }
+}
+
+template <bool kLds>
+__global__ __launch_bounds__(kSampT) void k_sip_fill(const float* __restrict__ S, int n,
+                                                    int n_forced, int n_qb, int H,
+                                                    double budget, uint64_t seed,
+                                                    const int32_t* __restrict__ row_ptr,
+                                                    const int32_t* __restrict__ status,
+                                                    int32_t* __restrict__ col_idx,
+                                                    float* __restrict__ logw) {
+  extern __shared__ __align__(16) float srow[];
+  __shared__ Red red;
+  __shared__ int wtot[kSampWaves];
+  if (*status != 0) return;  // plan exceeded its capacity: nothing is written
+  const int r = blockIdx.x;
+  const int qb = r % n_qb, bh = r / n_qb, h = bh % H, b = bh / H;
+  const float* s = stage_row<kLds>(S + (int64_t)r * n, n, srow);
+  const PiSolve ps = solve_pi(s, n, budget, red);
+  const int64_t start = row_ptr[r];
+  const int groups = (n + 3) / 4;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int run = 0;
+  for (int base = 0; base < groups; base += kSampT) {
+    const int g = base + t;
+    const uint32_t mask = g < groups ? draw_group(s, n, g, qb, h, b, seed, ps) : 0u;
+    const int k = __popc(mask);
+    int incl = k;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int up = __shfl_up(incl, o);
+      if (lane >= o) incl += up;
+    }
+    if (lane == 63) wtot[w] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int q = 0; q < kSampWaves; ++q) {
+      if (q < w) before += wtot[q];
+      tot += wtot[q];
+    }
+    int64_t pos = start + run + before + incl - k;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (mask & (1u << i)) {
+        const int j = 4 * g + i;
+        const double pi = pi_of(s[j], ps);
+        col_idx[pos] = j;
+        logw[pos] = pi == 1.0 ? 0.0f : (float)(-log(pi));
+        ++pos;
+      }
+    }
+    run += tot;
+    __syncthreads();
+  }
+  for (int i = t; i < n_forced; i += kSampT) {
+    col_idx[start + run + i] = n + i;
+    logw[start + run + i] = 0.0f;
+  }
+}
+
+constexpr size_t kSampLdsMax = 150 * 1024;
+
+template <bool kLds>
+static hipError_t launch_sampler_t(const Shape& s, const float* S, double budget, uint64_t seed,
+                                   int32_t* counts, int32_t* row_ptr, int32_t* col_idx,
+                                   float* logw, int64_t capacity, int32_t* status,
+                                   hipStream_t st) {
+  const size_t lds = kLds ? (size_t)s.n_kbs * sizeof(float) : 0;
+  const int n_forced = s.n_kb - s.n_kbs;
+  if (kLds) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_sip_count<kLds>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_sip_fill<kLds>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  k_sip_count<kLds><<<s.R, kSampT, lds, st>>>(S, s.n_kbs, n_forced, s.n_qb, s.H, budget, seed,
+                                              counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_scan<<<1, 1024, 0, st>>>(counts, s.R, row_ptr, capacity, status);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_sip_fill<kLds><<<s.R, kSampT, lds, st>>>(S, s.n_kbs, n_forced, s.n_qb, s.H, budget, seed,
+                                             row_ptr, status, col_idx, logw);
+  return hipGetLastError();
+}
+
+hipError_t launch_sampler(const Shape& s, const float* S, double budget, uint64_t seed,
+                          int32_t* counts, int32_t* row_ptr, int32_t* col_idx, float* logw,
+                          int64_t capacity, int32_t* status, hipStream_t st) {
+  if ((size_t)s.n_kbs * sizeof(float) <= kSampLdsMax)
+    return launch_sampler_t<true>(s, S, budget, seed, counts, row_ptr, col_idx, logw, capacity,
+                                  status, st);
+  return launch_sampler_t<false>(s, S, budget, seed, counts, row_ptr, col_idx, logw, capacity,
+                                 status, st);
+}
+
+}  // namespace abatt

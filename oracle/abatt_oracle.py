@@ -191,12 +191,16 @@ def ibcs_scores(Q: np.ndarray, K: np.ndarray, prob: Problem,
     """
     prob.check()
     rows = list(range(prob.R)) if rows is None else list(rows)
-    kbar = key_block_means(K, prob)
+    kbar = {}                       # key means of the heads the rows need
+    for r in rows:
+        b, h, _ = unflatten_row(prob, r)
+        if (b, h) not in kbar:
+            kbar[(b, h)] = key_block_means(K[b:b + 1, h:h + 1], prob)[0, 0]
     mu, w, counts = query_clusters(Q, prob, rows)
     S = np.empty((len(rows), prob.n_kbs), dtype=np.float64)
     for i, r in enumerate(rows):
         b, h, _ = unflatten_row(prob, r)
-        S[i] = block_scores(mu[i], w[i], kbar[b, h], prob.tau)
+        S[i] = block_scores(mu[i], w[i], kbar[(b, h)], prob.tau)
     return {"rows": rows, "kbar": kbar, "mu": mu, "w": w, "counts": counts,
             "S": S, "S32": S.astype(np.float32)}
 

@@ -1,0 +1,114 @@
+"""The C ABI on the CPU: the library loads without a GPU, exports what the
+header declares, sizes its buffers, and rejects bad arguments before any HIP
+call (so nothing here touches a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_09_amd as ab
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ab.load_library()
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "abatt.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(abatt_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = header_symbols()
+    assert len(syms) >= 12
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert sorted(ab.SYMBOLS) == syms
+    assert b"gfx950" in lib.abatt_version()
+
+
+def prob(**kw):
+    base = dict(B=1, H=2, N=1024, D=128, n_clusters=8, dtype="bf16")
+    base.update(kw)
+    return ab.Problem(**base)
+
+
+def test_sizes(lib):
+    p = prob()
+    assert ab.plan_rows(p) == 16
+    assert ab.max_nnz(p) == 16 * 256
+    b = ab.nnz_bound(p, 0.1)
+    assert 16 * 25.6 < b <= ab.max_nnz(p)
+    assert ab.nnz_bound(p, 1.0) == ab.max_nnz(p)
+    ws = ab.plan_workspace_bytes(p)
+    # means + centroids + weights + scores + counts, each 256-aligned
+    need = 2 * 256 * 128 * 4 + 16 * 8 * 128 * 4 + 16 * 8 * 4 + 16 * 256 * 4 + 16 * 4
+    assert need <= ws <= need + 5 * 256
+    assert ab.sampler_workspace_bytes(p) >= 16 * 4
+    pf = prob(N=1024 + 256, n_forced_tail=256)
+    assert ab.max_nnz(pf) == pf.R * (256 + 64)
+    assert ab.nnz_bound(pf, 0.1) - ab.nnz_bound(prob(N=1280, n_forced_tail=256), 0.1) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), -2), (dict(n_clusters=4), -2), (dict(q_block=64), -2),
+    (dict(kv_block=8), -2), (dict(N=0), -1), (dict(H=0), -1), (dict(N=1022), -1),
+    (dict(n_forced_tail=6), -1), (dict(scale=-1.0), -1), (dict(kmeans_iters=0), -1),
+])
+def test_bad_problems(lib, kw, code):
+    p = prob(**kw)
+    assert lib.abatt_plan_rows(ctypes.byref(p.c())) == -1
+    assert lib.abatt_plan_workspace_bytes(ctypes.byref(p.c())) == 0
+    fake = ctypes.c_void_p(0x1000)
+    pl = ab._Plan(0x1000, 0x1000, 0x1000, 10 ** 6, 0x1000)
+    r = lib.abatt_plan(ctypes.byref(p.c()), fake, fake, 0.1, 0, fake, 1 << 40,
+                       ctypes.byref(pl), None)
+    assert r == code
+
+
+def test_argument_checks_before_any_hip_call(lib):
+    p = prob()
+    c = p.c()
+    fake = ctypes.c_void_p(0x1000)
+    ws = ab.plan_workspace_bytes(p)
+    good = ab._Plan(0x1000, 0x1000, 0x1000, 10 ** 6, 0x1000)
+    P = ctypes.byref
+    # null tensors
+    assert lib.abatt_plan(P(c), None, fake, 0.1, 0, fake, ws, P(good), None) == -1
+    assert lib.abatt_attend(P(c), fake, None, fake, P(good), fake, None, None) == -1
+    assert lib.abatt_dense(P(c), fake, fake, fake, None, None, None) == -1
+    assert lib.abatt_key_means(P(c), None, fake, None) == -1
+    assert lib.abatt_scores(P(c), fake, fake, None, None, None, fake, ws, None) == -1
+    # budget outside (0, 1]
+    for b in (0.0, -0.1, 1.5, float("nan")):
+        assert lib.abatt_plan(P(c), fake, fake, b, 0, fake, ws, P(good), None) == -1
+        assert lib.abatt_plan_from_scores(P(c), fake, b, 0, fake, 1 << 20, P(good), None) == -1
+    # workspace too small
+    assert lib.abatt_plan(P(c), fake, fake, 0.1, 0, fake, ws - 1, P(good), None) == -3
+    assert lib.abatt_scores(P(c), fake, fake, fake, None, None, fake, ws - 1, None) == -3
+    assert lib.abatt_plan_from_scores(P(c), fake, 0.1, 0, fake, 3, P(good), None) == -3
+    # plan without status, or without arrays
+    nostat = ab._Plan(0x1000, 0x1000, 0x1000, 10 ** 6, None)
+    assert lib.abatt_plan(P(c), fake, fake, 0.1, 0, fake, ws, P(nostat), None) == -1
+    noarr = ab._Plan(None, 0x1000, 0x1000, 10 ** 6, 0x1000)
+    assert lib.abatt_attend(P(c), fake, fake, fake, P(noarr), fake, None, None) == -1
+    assert lib.abatt_attend(P(c), fake, fake, fake, None, fake, None, None) == -1
+    # capacity below the forced blocks
+    pf = prob(N=1280, n_forced_tail=256).c()
+    small = ab._Plan(0x1000, 0x1000, 0x1000, 10, 0x1000)
+    wsf = lib.abatt_plan_workspace_bytes(P(pf))
+    assert lib.abatt_plan(P(pf), fake, fake, 0.1, 0, fake, wsf, P(small), None) == -4
+    # dense accepts N not a multiple of 4 (keys past N are masked) but still checks D
+    assert lib.abatt_dense(P(prob(N=1023, D=96).c()), fake, fake, fake, fake, None, None) == -2
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert len(lib.abatt_status_str(code)) > 0
+    with pytest.raises(ab.AbattError):
+        ab._check(-1)

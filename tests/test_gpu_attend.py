@@ -1,0 +1,130 @@
+"""GPU parity of abatt_attend and abatt_dense against the CPU oracle.
+
+Plans come from the oracle (uploaded as CSR), so these tests isolate the
+attention kernels.  Bar: fp32 max-abs and mean-rel 1e-4; bf16 max-abs 1e-2 and
+mean-rel 1e-3 against the oracle's float64 output rounded to bf16.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import (LSE_TOL, TOL, check_output, lib_problem, oracle_problem, say, to_dev)
+from workloads import CONFIGS, Workload, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+ab = pytest.importorskip("block_sparse_attention_09_amd")
+
+CASES = {
+    # name: (workload, budget)
+    "tiny_f32": (CONFIGS["tiny"], 0.10),
+    "bf16_ragged": (Workload("r", B=1, H=2, D=128, grid=(3, 10, 12)), 0.10),
+    "bf16_many_chunks": (Workload("m", B=1, H=2, D=128, grid=(4, 16, 20)), 0.30),
+    "bf16_text": (Workload("x", B=1, H=2, D=128, grid=(2, 8, 16), n_text=16), 0.15),
+    "bf16_batch2_d64": (Workload("b", B=2, H=3, D=64, grid=(2, 12, 16)), 0.20),
+    "f32_d128": (Workload("f", B=1, H=1, D=128, grid=(2, 10, 12), dtype="f32", sigma=1.0), 0.2),
+}
+
+
+def _run(name, budget=None, seed=0):
+    wl, b0 = CASES[name]
+    budget = b0 if budget is None else budget
+    q, k, v = make_qkv(wl)
+    op = oracle_problem(wl)
+    pl = oracle.plan(q, k, op, budget, seed)
+    O, L = oracle.attend(q, k, v, pl, op)
+    say(f"{name} budget={budget} N={wl.N} nnz={len(pl.col_idx)}")
+    prob = lib_problem(wl)
+    dq, dk, dv = (to_dev(x, wl.dtype) for x in (q, k, v))
+    gp = ab.make_plan(pl.row_ptr, pl.col_idx, pl.logw, "cuda")
+    o, lse = ab.attend(dq, dk, dv, gp, problem=prob, return_lse=True)
+    torch.cuda.synchronize()
+    return wl, (q, k, v), op, (O, L), (o, lse), prob, (dq, dk, dv)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_attend_matches_oracle(name):
+    wl, _, _, (O, L), (o, lse), _, _ = _run(name)
+    check_output(o, O, wl.dtype, f"attend {name}")
+    lerr = np.abs(lse.cpu().numpy() - L).max()
+    say(f"attend {name}: lse max-abs {lerr:.3e}")
+    assert lerr <= LSE_TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "bf16_ragged", "bf16_text", "bf16_batch2_d64"])
+def test_budget_one_equals_dense(name):
+    wl, (q, k, v), op, (O, L), (o, lse), prob, (dq, dk, dv) = _run(name, budget=1.0)
+    Od, Ld = oracle.dense(q, k, v, op)
+    np.testing.assert_allclose(O, Od, rtol=1e-10, atol=1e-12)   # oracle: budget 1 == dense
+    check_output(o, Od, wl.dtype, f"attend@1 vs dense {name}")
+    od, lsed = ab.dense(dq, dk, dv, problem=prob, return_lse=True)
+    torch.cuda.synchronize()
+    check_output(od, Od, wl.dtype, f"dense {name}")
+    assert np.abs(lsed.cpu().numpy() - Ld).max() <= LSE_TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("N,dtype,D", [(1000, "bf16", 128), (1030, "bf16", 64), (333, "f32", 64),
+                                       (129, "bf16", 128)])
+def test_dense_ragged_lengths(N, dtype, D):
+    # dense accepts any N: the last key chunk and the last query block are partial
+    rng = np.random.default_rng(N)
+    shape = (1, 2, N, D)
+    q, k, v = (rng.standard_normal(shape).astype(np.float32) for _ in range(3))
+    if dtype == "bf16":
+        from workloads import round_like
+        q, k, v = (round_like(x, "bf16") for x in (q, k, v))
+    op = oracle.Problem(B=1, H=2, N=N, D=D)
+    Od, Ld = oracle.dense(q, k, v, op)
+    say(f"dense ragged N={N} {dtype} D={D}")
+    prob = ab.Problem(1, 2, N, D, dtype=dtype)
+    o, lse = ab.dense(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), problem=prob,
+                      return_lse=True)
+    torch.cuda.synchronize()
+    check_output(o, Od, dtype, f"dense N={N}")
+    assert np.abs(lse.cpu().numpy() - Ld).max() <= LSE_TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_empty_rows_invalid_ids_and_overflowed_plan(dtype):
+    wl = Workload("e", B=1, H=1, D=128 if dtype == "bf16" else 64, grid=(3, 8, 16), dtype=dtype)
+    q, k, v = make_qkv(wl)
+    op = oracle_problem(wl)
+    prob = lib_problem(wl)
+    R, nkb = op.R, op.n_kb
+    # row 0: empty; row 1: blocks incl. out-of-range ids (skipped); row 2..: a few blocks
+    rows = [[], [0, 5, nkb + 3, -1, 17], [1, 2, 3]] + [[4 * r, 4 * r + 1] for r in range(3, R)]
+    lws = [[], [0.0, 1.0, 9.0, 9.0, 0.5], [0.0, 0.0, 2.0]] + [[0.3, 0.0] for _ in range(3, R)]
+    rp = np.cumsum([0] + [len(x) for x in rows])
+    ci = np.array(sum(rows, []), np.int32)
+    lw = np.array(sum(lws, []), np.float32)
+    say(f"empty/invalid rows {dtype}")
+    gp = ab.make_plan(rp, ci, lw, "cuda")
+    dq, dk, dv = (to_dev(x, dtype) for x in (q, k, v))
+    o, lse = ab.attend(dq, dk, dv, gp, problem=prob, return_lse=True)
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    assert np.all(o[0, 0, :128] == 0) and np.all(np.isneginf(lse[0, 0, :128]))
+    valid = [(0, 0.0), (5, 1.0), (17, 0.5)]
+    ref, rl = oracle.attend_row(q, k, v, op, 1, np.array([c for c, _ in valid], np.int32),
+                                np.array([w for _, w in valid], np.float32))
+    check_output(torch.from_numpy(o[0, 0, 128:256]), ref, dtype, "row with invalid ids")
+    # a plan whose status says it overflowed: every row empty
+    gp.status = torch.ones(1, dtype=torch.int32, device="cuda")
+    o2, lse2 = ab.attend(dq, dk, dv, gp, problem=prob, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(o2 == 0) and torch.all(torch.isneginf(lse2))
+
+
+def test_attend_is_deterministic():
+    wl, b = CASES["bf16_many_chunks"]
+    q, k, v = make_qkv(wl)
+    op = oracle_problem(wl)
+    pl = oracle.plan(q, k, op, b, 0)
+    prob = lib_problem(wl)
+    dq, dk, dv = (to_dev(x, wl.dtype) for x in (q, k, v))
+    gp = ab.make_plan(pl.row_ptr, pl.col_idx, pl.logw, "cuda")
+    o1 = ab.attend(dq, dk, dv, gp, problem=prob)
+    o2 = ab.attend(dq, dk, dv, gp, problem=prob)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))

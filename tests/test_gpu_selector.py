@@ -1,0 +1,166 @@
+"""GPU parity of the selector and sampler kernels against the CPU oracle.
+
+* key means: to fp32 rounding;
+* k-means: per query block, identical cluster counts (weights) on >= 99% of
+  blocks, and centroids within 1e-4 relative where the counts agree (fp32
+  distances on the GPU vs float64 in the oracle can split a near tie);
+* scores: within 2e-3 relative (max) and 2e-4 (mean) on agreeing blocks;
+* sampler fed the oracle's fp32 scores: plan indices bit-exact, logw within
+  1 fp32 ulp (float64 log on both sides, rounded to fp32);
+* abatt_plan end to end: >= 99% block agreement (Jaccard over all rows).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import (jaccard, lib_problem, oracle_problem, plan_to_host, say, to_dev,
+                     ulp_diff_f32)
+from workloads import CONFIGS, Workload, make_qkv, random_scores
+
+pytestmark = pytest.mark.gpu
+
+ab = pytest.importorskip("block_sparse_attention_09_amd")
+
+SEL = {
+    "tiny_f32": CONFIGS["tiny"],
+    "bf16_ragged": Workload("r", B=1, H=2, D=128, grid=(3, 10, 12)),
+    "bf16_text_c16": Workload("x", B=1, H=2, D=128, grid=(2, 8, 16), n_text=16, n_clusters=16),
+    "bf16_d64_b2": Workload("b", B=2, H=2, D=64, grid=(2, 12, 16)),
+    "bf16_mid": Workload("m", B=1, H=2, D=128, grid=(6, 16, 24)),
+}
+
+
+@pytest.mark.parametrize("name", list(SEL))
+def test_key_means(name):
+    wl = SEL[name]
+    q, k, v = make_qkv(wl)
+    op = oracle_problem(wl)
+    ref = oracle.key_block_means(k, op)
+    say(f"key means {name}")
+    got = ab.key_means(to_dev(k, wl.dtype), lib_problem(wl))
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(got.cpu().numpy(), ref, rtol=2e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("name", list(SEL))
+def test_centroids_and_scores(name):
+    wl = SEL[name]
+    q, k, v = make_qkv(wl)
+    op = oracle_problem(wl)
+    sc = oracle.ibcs_scores(q, k, op)
+    say(f"scores {name} R={op.R} n_kbs={op.n_kbs}")
+    S, mu, w = ab.scores(to_dev(q, wl.dtype), to_dev(k, wl.dtype), lib_problem(wl))
+    torch.cuda.synchronize()
+    S, mu, w = S.cpu().numpy(), mu.cpu().numpy(), w.cpu().numpy()
+    same = np.all(np.abs(w - sc["w"]) <= 1e-6, axis=1)
+    say(f"  k-means blocks with identical weights: {same.mean():.4f}")
+    assert same.mean() >= 0.99
+    np.testing.assert_allclose(mu[same], sc["mu"][same], rtol=1e-4, atol=1e-4)
+    rel = np.abs(S[same] - sc["S"][same]) / sc["S"][same]
+    say(f"  score rel err max {rel.max():.3e} mean {rel.mean():.3e}")
+    assert rel.max() <= 2e-3 and rel.mean() <= 2e-4
+    np.testing.assert_allclose(S.sum(axis=1), 1.0, rtol=1e-4)
+
+
+SAMPLER = [
+    # (problem kwargs, budget, score spread, rows checked)
+    (dict(B=1, H=2, N=1024, D=64), 0.10, 3.0, None),
+    (dict(B=1, H=1, N=32760, D=128), 0.10, 4.0, None),
+    (dict(B=1, H=1, N=4096, D=128), 0.01, 2.0, None),
+    (dict(B=1, H=1, N=4096, D=128), 0.5, 1.0, None),
+    (dict(B=1, H=1, N=4096, D=128), 1.0, 2.0, None),
+    (dict(B=1, H=1, N=4096 + 256, D=128, n_forced_tail=256), 0.1, 3.0, None),
+    (dict(B=2, H=3, N=2048, D=128), 0.25, 6.0, None),
+    # n_kbs = 40000 > what fits in LDS: the global-memory variant
+    (dict(B=1, H=1, N=160000, D=128), 0.05, 3.0, [0, 1, 7, 500, 1249]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SAMPLER)))
+def test_sampler_bit_exact_from_oracle_scores(case):
+    kw, budget, spread, rows = SAMPLER[case]
+    op = oracle.Problem(**kw)
+    prob = ab.Problem(dtype="bf16", **kw)
+    S = random_scores(op.R, op.n_kbs, seed=case, spread=spread)
+    if case == 0:
+        S[:, ::7] = 0.0          # zero scores are never drawn
+    rows = list(range(op.R)) if rows is None else rows
+    ref = oracle.plan_from_scores(S[rows], op, budget, seed=1234 + case, rows=rows)
+    say(f"sampler case {case}: R={op.R} n_kbs={op.n_kbs} budget={budget}")
+    cap = ab.nnz_bound(prob, budget)
+    pl = ab.plan_from_scores(torch.from_numpy(S).cuda(), budget, 1234 + case, prob, capacity=cap)
+    torch.cuda.synchronize()
+    assert pl.ok()
+    rp, ci, lw = plan_to_host(pl)
+    for i, r in enumerate(rows):
+        a, b = ref.row_ptr[i], ref.row_ptr[i + 1]
+        ga, gb = rp[r], rp[r + 1]
+        np.testing.assert_array_equal(ci[ga:gb], ref.col_idx[a:b], err_msg=f"row {r}")
+        assert ulp_diff_f32(lw[ga:gb], ref.logw[a:b]).max(initial=0) <= 1, f"row {r}"
+    if len(rows) == op.R:
+        np.testing.assert_array_equal(rp, ref.row_ptr)
+
+
+def test_sampler_capacity_overflow_and_determinism():
+    kw = dict(B=1, H=1, N=4096, D=128)
+    prob = ab.Problem(dtype="bf16", **kw)
+    op = oracle.Problem(**kw)
+    S = torch.from_numpy(random_scores(op.R, op.n_kbs, seed=5)).cuda()
+    say("sampler overflow")
+    small = ab.plan_from_scores(S, 0.3, 7, prob, capacity=10)
+    a = ab.plan_from_scores(S, 0.3, 7, prob)
+    b = ab.plan_from_scores(S, 0.3, 7, prob)
+    torch.cuda.synchronize()
+    assert not small.ok()
+    assert small.nnz() == a.nnz() > 10      # row_ptr still reports the needed total
+    assert torch.equal(a.row_ptr, b.row_ptr)
+    n = a.nnz()
+    assert torch.equal(a.col_idx[:n], b.col_idx[:n]) and torch.equal(a.logw[:n], b.logw[:n])
+
+
+@pytest.mark.parametrize("name", list(SEL))
+def test_plan_end_to_end_agreement(name):
+    wl = SEL[name]
+    q, k, v = make_qkv(wl)
+    op = oracle_problem(wl)
+    budget = 0.12
+    ref = oracle.plan(q, k, op, budget, seed=3)
+    say(f"plan e2e {name}")
+    dq, dk = to_dev(q, wl.dtype), to_dev(k, wl.dtype)
+    prob = lib_problem(wl)
+    pl = ab.plan(dq, dk, budget, seed=3, problem=prob)
+    pl2 = ab.plan(dq, dk, budget, seed=3, problem=prob)
+    torch.cuda.synchronize()
+    assert pl.ok()
+    rp, ci, lw = plan_to_host(pl)
+    rp2, ci2, lw2 = plan_to_host(pl2)
+    np.testing.assert_array_equal(rp, rp2)          # deterministic
+    np.testing.assert_array_equal(ci, ci2)
+    jac = jaccard(rp, ci, ref.row_ptr, ref.col_idx)
+    say(f"  jaccard {jac:.5f} nnz gpu {len(ci)} oracle {len(ref.col_idx)}")
+    assert jac >= 0.99
+    # forced blocks present in every row
+    nf = op.n_kb - op.n_kbs
+    for r in range(op.R):
+        row = ci[rp[r]:rp[r + 1]]
+        assert np.all(np.diff(row) > 0)
+        if nf:
+            np.testing.assert_array_equal(row[-nf:], np.arange(op.n_kbs, op.n_kb))
+
+
+def test_plan_then_attend_budget_one():
+    wl = SEL["bf16_ragged"]
+    q, k, v = make_qkv(wl)
+    op = oracle_problem(wl)
+    say("plan budget 1 -> attend == dense")
+    prob = lib_problem(wl)
+    dq, dk, dv = (to_dev(x, wl.dtype) for x in (q, k, v))
+    pl = ab.plan(dq, dk, 1.0, seed=0, problem=prob)
+    o = ab.attend(dq, dk, dv, pl, problem=prob)
+    torch.cuda.synchronize()
+    assert pl.nnz() == op.R * op.n_kb
+    assert torch.all(pl.logw[:pl.nnz()] == 0)
+    from helpers import check_output
+    Od, _ = oracle.dense(q, k, v, op)
+    check_output(o, Od, wl.dtype, "plan@1 + attend vs dense")
