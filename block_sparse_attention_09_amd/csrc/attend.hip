@@ -16,9 +16,11 @@
 //     needs a single exchange between the two half-waves;
 //   * keys arrive in chunks of 16 kept blocks = 64 keys.  Each 4-token block
 //     of a head is 4*D*2 contiguous bytes, so one wave-wide 16-byte load
-//     gathers a whole block (D=128) into the K tile.  V is written to LDS
-//     transposed and converted to fp16 (exact for bf16 values in fp16's
-//     normal range) so that PV can run as O^T = V^T P^T on fp16 MFMA with
+//     gathers a whole block (D=128) into the K tile.  The block ids of a
+//     chunk are fetched once per wave and broadcast with readlane.  V is
+//     converted to fp16 while it is staged (exact for bf16 values in fp16's
+//     normal range) and stored row-major; the PV operand is read with the
+//     gfx950 LDS transpose read, so PV runs as O^T = V^T P^T on fp16 MFMA with
 //     the probabilities straight from the softmax registers: the key order
 //     inside an MFMA k-step is chosen to match what each lane already holds;
 //   * two LDS buffers, global loads for chunk c+1 issued before chunk c is
@@ -37,6 +39,25 @@ namespace abatt {
 
 constexpr float kRescaleLog2 = 8.0f;
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// gfx950 LDS transpose read: within each 16-lane group, lane r supplies the
+// address of 4 consecutive 16-bit elements; lane i receives element i%4 of the
+// lanes 4k + i/4 (k = 0..3).  With lane r pointing at row k0 + r/4, columns
+// c0 + 4*(r%4) of a row-major tile, lane i gets column c0 + i of rows
+// k0..k0+3 -- the K-contiguous operand layout of a 32x32x16 MFMA.
+__device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p));
+}
+
+// V tile swizzle: 16-byte chunk c of row r is stored at chunk c ^ vswz(r), so
+// the four rows a transpose read touches fall on different banks.
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  return (4 * (row & 3)) & (D / 8 - 1);
+}
+
 template <int D, bool kGather>
 __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -46,18 +67,19 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     int n_qb, int n_kb, int R, float scale_log2) {
   constexpr int KS = D / 16;          // QK^T k-steps
   constexpr int DT = D / 32;          // PV output tiles
-  constexpr int KROW = D + 8;         // K tile row stride (bf16)
-  constexpr int VROW = 64 + 4;        // V^T tile row stride (fp16)
-  constexpr int SLOTS = 2 * D / 64;   // per-lane load slots per chunk
-  constexpr int HALF = D / 2;         // 16-byte K chunks (and V d-pairs) per block
+  constexpr int KROW = D + 8;         // K tile row stride (bf16), padded
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int SLOTS = 2 * D / 64;   // 16-byte loads per lane per chunk, for K and for V
+  constexpr int BPS = 64 / (4 * CPR); // blocks covered by one slot of a wave (1 or 2)
   __shared__ __align__(16) uint16_t Ks[2][64 * KROW];
-  __shared__ __align__(16) uint16_t Vt[2][D * VROW];
-  __shared__ __align__(16) float lw2[2][64];
+  __shared__ __align__(16) uint16_t Vs[2][64 * D];
+  __shared__ float lwb[2][16];
 
   const int r = xcd_remap(blockIdx.x, R);
   const int qb = r % n_qb;
   const int64_t bh = r / n_qb;
-  const int t = threadIdx.x, wv = t >> 6, lane = t & 63, l32 = lane & 31, hh = lane >> 5;
+  const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
 
   int64_t start = 0;
   int nblk;
@@ -84,75 +106,59 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
       qreg[s] = bf16x8{};
   }
 
-  // block id of block bi (0..15) of chunk c; lw gets its log2-domain shift
-  auto block_of = [&](int c, int bi, float& lw) -> int {
-    const int idx = c * 16 + bi;
+  // block ids of a chunk: lane j holds block 16c + (j & 15), branch-free
+  auto fetch_ids = [&](int c, int& id, float& lw) {
+    const int idx = 16 * c + (lane & 15);
     if constexpr (kGather) {
-      if (idx < nblk) {
-        const int id = col_idx[start + idx];
-        if (id >= 0 && id < n_kb) {
-          lw = logw[start + idx] * kLog2e;
-          return id;
-        }
-      }
-      lw = -INFINITY;
-      return 0;
+      const int64_t at = start + (idx < nblk ? idx : nblk - 1);
+      const int raw = col_idx[at];
+      const float lwr = logw[at];
+      const bool ok = idx < nblk && raw >= 0 && raw < n_kb;
+      id = ok ? raw : 0;
+      lw = ok ? lwr * kLog2e : -INFINITY;
     } else {
+      id = idx;
       lw = 0.f;
-      return idx;
     }
   };
-  auto token = [&](int id, int k) -> int64_t {
-    const int tok = 4 * id + k;
-    if constexpr (kGather) return tok;
-    return tok < N ? tok : N - 1;
-  };
 
-  u32x4 kpre[SLOTS];
-  uint32_t vpre[SLOTS][4];
-  float lwpre = 0.f;
+  u32x4 kpre[SLOTS], vpre[SLOTS];
+  int idn = 0;
+  float lwn = 0.f;
+  // lane -> (block within the slot, key within the block, 16-byte chunk)
+  const int sub = lane / (4 * CPR);
+  const int key = (lane % (4 * CPR)) / CPR;
+  const int dc = lane % CPR;
 
   auto load_chunk = [&](int c) {
+    fetch_ids(c, idn, lwn);
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
-      const int lin = i * 64 + lane;
-      const int bi = 4 * wv + lin / HALF;
-      const int rem = lin % HALF;
-      float lw;
-      const int id = block_of(c, bi, lw);
-      const int key = rem / (D / 8), dc = rem % (D / 8);
-      kpre[i] = *reinterpret_cast<const u32x4*>(Kh + token(id, key) * D + 8 * dc);
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        vpre[i][k] = *reinterpret_cast<const uint32_t*>(Vh + token(id, k) * D + 2 * rem);
-    }
-    if (t < 64) {
-      float lw;
-      const int id = block_of(c, t >> 2, lw);
-      if constexpr (!kGather) lw = (4 * id + (t & 3) < N) ? 0.f : -INFINITY;
-      lwpre = lw;
+      const int bi = 4 * wv + i * BPS;
+      int id = __builtin_amdgcn_readlane(idn, bi);
+      if constexpr (BPS == 2) {
+        const int id1 = __builtin_amdgcn_readlane(idn, bi + 1);
+        id = sub ? id1 : id;
+      }
+      int64_t tok = 4 * (int64_t)id + key;
+      if constexpr (!kGather) tok = tok < N ? tok : N - 1;
+      kpre[i] = *reinterpret_cast<const u32x4*>(Kh + tok * D + 8 * dc);
+      vpre[i] = *reinterpret_cast<const u32x4*>(Vh + tok * D + 8 * dc);
     }
   };
   auto store_chunk = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
-      const int lin = i * 64 + lane;
-      const int bi = 4 * wv + lin / HALF;
-      const int rem = lin % HALF;
-      const int key = rem / (D / 8), dc = rem % (D / 8);
-      *reinterpret_cast<u32x4*>(&Ks[buf][(4 * bi + key) * KROW + 8 * dc]) = kpre[i];
-      // V^T: rows 2*rem (even dim) and 2*rem+1 (odd dim), columns 4*bi..4*bi+3
-      const uint32_t* v = vpre[i];
-      const u32x2 ev = {pack_f16_rtz(__uint_as_float(v[0] << 16), __uint_as_float(v[1] << 16)),
-                        pack_f16_rtz(__uint_as_float(v[2] << 16), __uint_as_float(v[3] << 16))};
-      const u32x2 od = {pack_f16_rtz(__uint_as_float(v[0] & 0xffff0000u),
-                                     __uint_as_float(v[1] & 0xffff0000u)),
-                        pack_f16_rtz(__uint_as_float(v[2] & 0xffff0000u),
-                                     __uint_as_float(v[3] & 0xffff0000u))};
-      *reinterpret_cast<u32x2*>(&Vt[buf][(2 * rem) * VROW + 4 * bi]) = ev;
-      *reinterpret_cast<u32x2*>(&Vt[buf][(2 * rem + 1) * VROW + 4 * bi]) = od;
+      const int row = 4 * (4 * wv + i * BPS + sub) + key;
+      *reinterpret_cast<u32x4*>(&Ks[buf][row * KROW + 8 * dc]) = kpre[i];
+      u32x4 hv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        hv[e] = pack_f16_rtz(__uint_as_float(vpre[i][e] << 16),
+                             __uint_as_float(vpre[i][e] & 0xffff0000u));
+      *reinterpret_cast<u32x4*>(&Vs[buf][row * D + 8 * (dc ^ vswz<D>(row))]) = hv;
     }
-    if (t < 64) lw2[buf][t] = lwpre;
+    if (t < 16) lwb[buf][t] = lwn;
   };
 
   f32x16 oacc[DT];
@@ -166,11 +172,15 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   }
   __syncthreads();
 
+  // transpose-read geometry (per lane, fixed)
+  const int tr_r = lane & 15;
+  const int tr_g = (lane >> 4) & 1;
+
   for (int c = 0; c < nchunk; ++c) {
     const int buf = c & 1;
     if (c + 1 < nchunk) load_chunk(c + 1);
 
-    // S^T tile: lane holds query l32, keys 32*tt + 8*(v/4) + 4*hh + v%4
+    // S^T tile: lane holds query l32, keys 32*tt + 8*g + 4*hh + (0..3) = block 8tt+2g+hh
     f32x16 sacc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -182,25 +192,32 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
         sacc[tt] = mfma_bf16_32x32x16(a, qreg[s], sacc[tt]);
       }
     }
-    float x[32];
+    if constexpr (!kGather) {
+      if (c == nchunk - 1) {  // keys past N in the last dense chunk
+        const int base = 64 * c;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (base + 32 * tt + 8 * (v >> 2) + 4 * hh + (v & 3) >= N) sacc[tt][v] = -INFINITY;
+      }
+    }
+    float lwg[8];
     float mloc = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 sh = *reinterpret_cast<const f32x4*>(&lw2[buf][32 * tt + 8 * g + 4 * hh]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float z = fmaf(sacc[tt][4 * g + q], scale_log2, sh[q]);
-          x[16 * tt + 4 * g + q] = z;
-          mloc = fmaxf(mloc, z);
-        }
+        lwg[4 * tt + g] = lwb[buf][8 * tt + 2 * g + hh];
+        const float gm = fmaxf(fmaxf(sacc[tt][4 * g], sacc[tt][4 * g + 1]),
+                               fmaxf(sacc[tt][4 * g + 2], sacc[tt][4 * g + 3]));
+        mloc = fmaxf(mloc, fmaf(gm, scale_log2, lwg[4 * tt + g]));
       }
     }
     const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32));
     const bool need = mrow > m_used + kRescaleLog2;
     if (__any(need)) {
-      const float alpha = need ? exp2f(m_used - mrow) : 1.f;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_used - mrow) : 1.f;
       if (need) m_used = mrow;
       lsum *= alpha;
 #pragma unroll
@@ -209,13 +226,21 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     const float mref = m_used == -INFINITY ? 0.f : m_used;
     uint32_t pk[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p0 = exp2f(x[2 * i] - mref), p1 = exp2f(x[2 * i + 1] - mref);
-      lsum += p0 + p1;
-      pk[i] = pack_f16_rne(p0, p1);
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float sh = lwg[4 * tt + g] - mref;
+        float p[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          p[q] = __builtin_amdgcn_exp2f(fmaf(sacc[tt][4 * g + q], scale_log2, sh));
+        lsum += (p[0] + p[1]) + (p[2] + p[3]);
+        pk[8 * tt + 2 * g] = pack_f16_rne(p[0], p[1]);
+        pk[8 * tt + 2 * g + 1] = pack_f16_rne(p[2], p[3]);
+      }
     }
-    // O^T += V^T P^T; k-step (tt, gp) covers keys 32tt+16gp .. +15 in the
-    // order lane-half hh holds them: 4hh+{0..3}, 8+4hh+{0..3}
+    // O^T += V^T P^T.  k-step (tt, gp) covers keys 32tt+16gp .. +15 in the order
+    // lane-half hh holds them: 4hh+{0..3}, then 8+4hh+{0..3}.
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
@@ -223,12 +248,16 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
         const int pb = 8 * tt + 4 * gp;
         const f16x8 pop =
             __builtin_bit_cast(f16x8, u32x4{pk[pb], pk[pb + 1], pk[pb + 2], pk[pb + 3]});
+        const int rowa = 32 * tt + 16 * gp + 4 * hh + (tr_r >> 2);
+        const int rowb = rowa + 8;
 #pragma unroll
         for (int u = 0; u < DT; ++u) {
-          const uint16_t* row = &Vt[buf][(32 * u + l32) * VROW + 32 * tt + 16 * gp + 4 * hh];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 8);
-          const f16x8 vop = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          const int d0 = 32 * u + 16 * tr_g + 4 * (tr_r & 3);
+          const v4i16 va = lds_read_tr16(&Vs[buf][rowa * D + 8 * ((d0 >> 3) ^ vswz<D>(rowa)) + (d0 & 7)]);
+          const v4i16 vb = lds_read_tr16(&Vs[buf][rowb * D + 8 * ((d0 >> 3) ^ vswz<D>(rowb)) + (d0 & 7)]);
+          const f16x8 vop = __builtin_bit_cast(
+              f16x8, u32x4{__builtin_bit_cast(u32x2, va)[0], __builtin_bit_cast(u32x2, va)[1],
+                           __builtin_bit_cast(u32x2, vb)[0], __builtin_bit_cast(u32x2, vb)[1]});
           oacc[u] = mfma_f16_32x32x16(vop, pop, oacc[u]);
         }
       }
@@ -345,14 +374,14 @@ __global__ __launch_bounds__(128) void k_attend_f32(
     }
     const float mn = fmaxf(m, cm);
     if (mn == -INFINITY) continue;
-    const float alpha = exp2f(m - mn);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
     m = mn;
     l *= alpha;
 #pragma unroll
     for (int e = 0; e < D; ++e) o[e] *= alpha;
 #pragma unroll
     for (int k = 0; k < CK; ++k) {
-      const float p = exp2f(z[k] - m);
+      const float p = __builtin_amdgcn_exp2f(z[k] - m);
       l += p;
 #pragma unroll
       for (int e = 0; e < D; e += 4) {

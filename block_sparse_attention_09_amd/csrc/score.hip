@@ -134,11 +134,11 @@ __global__ __launch_bounds__(256, 2) void k_scores(const float* __restrict__ mu,
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     if (tmax > m_run) {
-      s_run *= exp2f(m_run - tmax);
+      s_run *= __builtin_amdgcn_exp2f(m_run - tmax);
       m_run = tmax;
     }
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s_run += exp2f(x[v] - m_run);
+    for (int v = 0; v < 16; ++v) s_run += __builtin_amdgcn_exp2f(x[v] - m_run);
     if (tile + 1 < n_tiles) store_tile(buf ^ 1);
     __syncthreads();
   }
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256, 2) void k_scores(const float* __restrict__ mu,
     // lane: key 32*tile + l32, centroid rows 32*wv + 8*(v/4) + 4*hh + v%4
     float p[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) p[v] = exp2f(big[v] + small[v] + a_v[v]);
+    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(big[v] + small[v] + a_v[v]);
     const int key = 32 * tile + l32;
     if constexpr (C == 8) {
       // rows 8g..8g+7 of the wave = one query block; this half holds 4 of them
