@@ -28,9 +28,14 @@ FLAGS = [
 ]
 
 
+# per-file flags: the attention kernels never see NaN by construction, and
+# without NaN semantics fmax needs no canonicalising moves around MFMA results
+FILE_FLAGS = {"attend.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

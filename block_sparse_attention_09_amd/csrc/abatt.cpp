@@ -1,7 +1,7 @@
 // C ABI of libabatt: argument checks, workspace layout, kernel launches.
 // Every check runs on the host before any HIP call, so invalid arguments come
 // back as a status code with nothing enqueued (and without a GPU present).
-#include "../../include/abatt.h"
+#include "abatt.h"
 
 #include <cmath>
 #include <cstring>
@@ -35,6 +35,8 @@ abatt_status make_shape(const abatt_problem_t* p, Shape* s) {
   const int64_t n_qb = (p->N + p->q_block - 1) / p->q_block;
   const int64_t R = (int64_t)p->B * p->H * n_qb;
   if (R > INT32_MAX / 2) return ABATT_EUNSUPPORTED;
+  // one head of K or V is addressed through a 32-bit buffer range
+  if ((int64_t)p->N * p->D * 4 > INT32_MAX) return ABATT_EUNSUPPORTED;
   s->B = p->B;
   s->H = p->H;
   s->N = p->N;

@@ -28,8 +28,8 @@
 //   * online softmax in the exp2 domain; the running max is only moved when
 //     a chunk raises it by more than 8 (log2 units), so most chunks skip the
 //     rescale of the accumulators (p then stays below 2^8, fine for fp16);
-//   * work-groups are remapped so consecutive query blocks of a head share an
-//     XCD (and its L2), which is where gathered K/V blocks get reused.
+//   * work-groups run in plan-row order, so all XCDs share one head at a time
+//     and its K/V stays resident in the Infinity Cache.
 // fp32 kernel: plain fp32 arithmetic (one thread per query), used for fp32
 // problems.
 #include "common.h"
@@ -58,6 +58,13 @@ __device__ __forceinline__ int vswz(int row) {
   return (4 * (row & 3)) & (D / 8 - 1);
 }
 
+// Buffer resource for a head's K or V (bounds-checked: loads past the end
+// return zero, which the dense path relies on for its last partial block).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, bytes,
+                                           0x00020000);
+}
+
 template <int D, bool kGather>
 __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -71,11 +78,17 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int SLOTS = 2 * D / 64;   // 16-byte loads per lane per chunk, for K and for V
   constexpr int BPS = 64 / (4 * CPR); // blocks covered by one slot of a wave (1 or 2)
+  constexpr int BLOCK_BYTES = 4 * D * 2;
   __shared__ __align__(16) uint16_t Ks[2][64 * KROW];
   __shared__ __align__(16) uint16_t Vs[2][64 * D];
   __shared__ float lwb[2][16];
 
-  const int r = xcd_remap(blockIdx.x, R);
+  // Plan rows in launch order: the dispatcher deals consecutive work-groups to
+  // the 8 XCDs in turn, so all XCDs work on the same head at once and that
+  // head's K/V (38.7 MB at 75600 tokens) stays in the 256 MB Infinity Cache.
+  // (Giving each XCD its own contiguous rows raised the L2 hit rate but
+  // spread the XCDs over 8 heads, and measured slower.)
+  const int r = blockIdx.x;
   const int qb = r % n_qb;
   const int64_t bh = r / n_qb;
   const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hh = lane >> 5;
@@ -93,8 +106,8 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   }
   const int nchunk = (nblk + 15) / 16;
 
-  const uint16_t* Kh = K + bh * N * D;
-  const uint16_t* Vh = V + bh * N * D;
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(K + bh * N * D, N * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(V + bh * N * D, N * D * 2);
 
   const int qrow = qb * 128 + 32 * wv + l32;
   bf16x8 qreg[KS];
@@ -111,39 +124,49 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     const int idx = 16 * c + (lane & 15);
     if constexpr (kGather) {
       const int64_t at = start + (idx < nblk ? idx : nblk - 1);
-      const int raw = col_idx[at];
-      const float lwr = logw[at];
-      const bool ok = idx < nblk && raw >= 0 && raw < n_kb;
-      id = ok ? raw : 0;
-      lw = ok ? lwr * kLog2e : -INFINITY;
+      id = col_idx[at];
+      lw = logw[at];
     } else {
       id = idx;
       lw = 0.f;
     }
   };
+  // validity is applied when the ids are used (keeps the loads in flight)
+  auto valid_id = [&](int c, int raw) -> bool {
+    if constexpr (kGather) return 16 * c + (lane & 15) < nblk && raw >= 0 && raw < n_kb;
+    return true;
+  };
 
-  u32x4 kpre[SLOTS], vpre[SLOTS];
-  int idn = 0;
-  float lwn = 0.f;
   // lane -> (block within the slot, key within the block, 16-byte chunk)
   const int sub = lane / (4 * CPR);
   const int key = (lane % (4 * CPR)) / CPR;
   const int dc = lane % CPR;
+  const int lane_off = (key * D + 8 * dc) * 2;
 
-  auto load_chunk = [&](int c) {
-    fetch_ids(c, idn, lwn);
+  u32x4 kpre[SLOTS], vpre[SLOTS];
+  int id_next = 0, id_far = 0;       // raw ids of chunks c+1 and c+2
+  float lw_next = 0.f, lw_far = 0.f;
+  float lw_store = 0.f;
+
+  auto issue_loads = [&](int c) {    // K/V of chunk c, from id_next
+    const bool ok = valid_id(c, id_next);
+    const int idv = ok ? id_next : 0;
+    lw_store = ok ? lw_next * kLog2e : -INFINITY;
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
       const int bi = 4 * wv + i * BPS;
-      int id = __builtin_amdgcn_readlane(idn, bi);
-      if constexpr (BPS == 2) {
-        const int id1 = __builtin_amdgcn_readlane(idn, bi + 1);
-        id = sub ? id1 : id;
+      int voff, soff;
+      if constexpr (BPS == 1) {
+        soff = __builtin_amdgcn_readlane(idv, bi) * BLOCK_BYTES;
+        voff = lane_off;
+      } else {
+        const int id0 = __builtin_amdgcn_readlane(idv, bi);
+        const int id1 = __builtin_amdgcn_readlane(idv, bi + 1);
+        soff = 0;
+        voff = (sub ? id1 : id0) * BLOCK_BYTES + lane_off;
       }
-      int64_t tok = 4 * (int64_t)id + key;
-      if constexpr (!kGather) tok = tok < N ? tok : N - 1;
-      kpre[i] = *reinterpret_cast<const u32x4*>(Kh + tok * D + 8 * dc);
-      vpre[i] = *reinterpret_cast<const u32x4*>(Vh + tok * D + 8 * dc);
+      kpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff, soff, 0));
+      vpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, soff, 0));
     }
   };
   auto store_chunk = [&](int buf) {
@@ -158,17 +181,34 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
                              __uint_as_float(vpre[i][e] & 0xffff0000u));
       *reinterpret_cast<u32x4*>(&Vs[buf][row * D + 8 * (dc ^ vswz<D>(row))]) = hv;
     }
-    if (t < 16) lwb[buf][t] = lwn;
+    if (t < 16) lwb[buf][t] = lw_store;
   };
 
   f32x16 oacc[DT];
 #pragma unroll
   for (int u = 0; u < DT; ++u) oacc[u] = f32x16{};
-  float m_used = -INFINITY, lsum = 0.f;
+  float m_used = -INFINITY;
+  float lsum0 = 0.f, lsum1 = 0.f;
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
+  // Pipeline: chunk c is computed from LDS stage c%2 while the registers carry
+  // chunk c+1 (loaded during the previous iteration) and the block ids of
+  // chunk c+2 are in flight.  At the top of iteration c the registers go to
+  // stage (c+1)%2 (free since the barrier that ended iteration c-1), then the
+  // loads of chunk c+2 are issued, so every gather load has a whole iteration
+  // to land.  Chunk indices are clamped to the last chunk so the prefetch code
+  // runs unconditionally (no branch merges that would force early waits); the
+  // cost is a few redundant loads at the end.
+  const int clast = nchunk > 0 ? nchunk - 1 : 0;
   if (nchunk > 0) {
-    load_chunk(0);
+    fetch_ids(0, id_next, lw_next);
+    issue_loads(0);
+    fetch_ids(min(1, clast), id_far, lw_far);
     store_chunk(0);
+    id_next = id_far;
+    lw_next = lw_far;
+    issue_loads(min(1, clast));
+    fetch_ids(min(2, clast), id_far, lw_far);
   }
   __syncthreads();
 
@@ -178,15 +218,18 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
 
   for (int c = 0; c < nchunk; ++c) {
     const int buf = c & 1;
-    if (c + 1 < nchunk) load_chunk(c + 1);
+    store_chunk(buf ^ 1);             // chunk c+1 (registers) -> free stage
+    id_next = id_far;
+    lw_next = lw_far;
+    issue_loads(min(c + 2, clast));   // chunk c+2 -> registers
+    fetch_ids(min(c + 3, clast), id_far, lw_far);
 
     // S^T tile: lane holds query l32, keys 32*tt + 8*g + 4*hh + (0..3) = block 8tt+2g+hh
-    f32x16 sacc[2];
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      sacc[tt] = f32x16{};
+    for (int s = 0; s < KS; ++s) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
+      for (int tt = 0; tt < 2; ++tt) {
         const bf16x8 a =
             *reinterpret_cast<const bf16x8*>(&Ks[buf][(32 * tt + l32) * KROW + 16 * s + 8 * hh]);
         sacc[tt] = mfma_bf16_32x32x16(a, qreg[s], sacc[tt]);
@@ -219,7 +262,8 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     if (__any(need)) {
       const float alpha = need ? __builtin_amdgcn_exp2f(m_used - mrow) : 1.f;
       if (need) m_used = mrow;
-      lsum *= alpha;
+      lsum0 *= alpha;
+      lsum1 *= alpha;
 #pragma unroll
       for (int u = 0; u < DT; ++u) oacc[u] *= alpha;
     }
@@ -234,9 +278,11 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           p[q] = __builtin_amdgcn_exp2f(fmaf(sacc[tt][4 * g + q], scale_log2, sh));
-        lsum += (p[0] + p[1]) + (p[2] + p[3]);
         pk[8 * tt + 2 * g] = pack_f16_rne(p[0], p[1]);
         pk[8 * tt + 2 * g + 1] = pack_f16_rne(p[2], p[3]);
+        // the row sum uses the same fp16 probabilities as the numerator
+        lsum0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[8 * tt + 2 * g]), ones, lsum0, false);
+        lsum1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[8 * tt + 2 * g + 1]), ones, lsum1, false);
       }
     }
     // O^T += V^T P^T.  k-step (tt, gp) covers keys 32tt+16gp .. +15 in the order
@@ -262,11 +308,11 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
         }
       }
     }
-    if (c + 1 < nchunk) store_chunk(buf ^ 1);
     __syncthreads();
   }
 
   // epilogue: O^T lane layout = query l32, dims 32u + 8g + 4hh + (0..3)
+  const float lsum = lsum0 + lsum1;
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (qrow < N) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;

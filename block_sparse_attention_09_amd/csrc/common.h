@@ -23,9 +23,9 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
 
 // float -> bfloat16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (u & 0x7fffffffu) > 0x7f800000u ? ((u >> 16) | 0x40u) : rne;
 }
 
 // Two floats -> packed fp16 pair, round to nearest even.
