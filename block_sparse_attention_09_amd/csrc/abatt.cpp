@@ -71,7 +71,7 @@ abatt_status make_dense_shape(const abatt_problem_t* p, Shape* s) {
 }
 
 struct PlanWs {
-  size_t kmean, mu, w, S, counts, total;
+  size_t kmean, mu, w, S, sampler, total;
 };
 
 PlanWs plan_ws_layout(const Shape& s) {
@@ -85,13 +85,13 @@ PlanWs plan_ws_layout(const Shape& s) {
   off = align_up(off + (size_t)s.R * s.n_clusters * sizeof(float));
   l.S = off;
   off = align_up(off + (size_t)s.R * s.n_kbs * sizeof(float));
-  l.counts = off;
-  off = align_up(off + (size_t)s.R * sizeof(int32_t));
+  l.sampler = off;
+  off = align_up(off + abatt::sampler_ws_layout(s).total);
   l.total = off;
   return l;
 }
 
-size_t sampler_ws_bytes(const Shape& s) { return align_up((size_t)s.R * sizeof(int32_t)); }
+size_t sampler_ws_bytes(const Shape& s) { return align_up(abatt::sampler_ws_layout(s).total); }
 
 abatt_status hip_status(hipError_t e) { return e == hipSuccess ? ABATT_OK : ABATT_EHIP; }
 
@@ -161,12 +161,12 @@ abatt_status abatt_scores(const abatt_problem_t* p, const void* Q, const void* K
   const PlanWs l = plan_ws_layout(s);
   if (workspace_bytes < l.total) return ABATT_EWORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  float* kmean = reinterpret_cast<float*>(ws + l.kmean);
+  uint16_t* kplanes = reinterpret_cast<uint16_t*>(ws + l.kmean);
   float* mu = centroids ? centroids : reinterpret_cast<float*>(ws + l.mu);
   float* w = weights ? weights : reinterpret_cast<float*>(ws + l.w);
-  hipError_t e = abatt::launch_key_means(s, K, kmean, stream);
+  hipError_t e = abatt::launch_key_means_split(s, K, kplanes, stream);
   if (e == hipSuccess) e = abatt::launch_kmeans(s, Q, mu, w, stream);
-  if (e == hipSuccess) e = abatt::launch_scores(s, mu, w, kmean, S, stream);
+  if (e == hipSuccess) e = abatt::launch_scores(s, mu, w, kplanes, S, stream);
   return hip_status(e);
 }
 
@@ -181,8 +181,7 @@ abatt_status abatt_plan_from_scores(const abatt_problem_t* p, const float* S, do
   if (st != ABATT_OK) return st;
   if (workspace_bytes < sampler_ws_bytes(s)) return ABATT_EWORKSPACE;
   if (plan->capacity < (int64_t)s.R * (s.n_kb - s.n_kbs)) return ABATT_ECAPACITY;
-  int32_t* counts = static_cast<int32_t*>(workspace);
-  return hip_status(abatt::launch_sampler(s, S, budget, seed, counts, plan->row_ptr,
+  return hip_status(abatt::launch_sampler(s, S, budget, seed, workspace, plan->row_ptr,
                                           plan->col_idx, plan->logw, plan->capacity,
                                           plan->status, stream));
 }
@@ -201,16 +200,15 @@ abatt_status abatt_plan(const abatt_problem_t* p, const void* Q, const void* K, 
   if (workspace_bytes < l.total) return ABATT_EWORKSPACE;
   if (plan->capacity < (int64_t)s.R * (s.n_kb - s.n_kbs)) return ABATT_ECAPACITY;
   char* ws = static_cast<char*>(workspace);
-  float* kmean = reinterpret_cast<float*>(ws + l.kmean);
+  uint16_t* kplanes = reinterpret_cast<uint16_t*>(ws + l.kmean);
   float* mu = reinterpret_cast<float*>(ws + l.mu);
   float* w = reinterpret_cast<float*>(ws + l.w);
   float* S = reinterpret_cast<float*>(ws + l.S);
-  int32_t* counts = reinterpret_cast<int32_t*>(ws + l.counts);
-  hipError_t e = abatt::launch_key_means(s, K, kmean, stream);
+  hipError_t e = abatt::launch_key_means_split(s, K, kplanes, stream);
   if (e == hipSuccess) e = abatt::launch_kmeans(s, Q, mu, w, stream);
-  if (e == hipSuccess) e = abatt::launch_scores(s, mu, w, kmean, S, stream);
+  if (e == hipSuccess) e = abatt::launch_scores(s, mu, w, kplanes, S, stream);
   if (e == hipSuccess)
-    e = abatt::launch_sampler(s, S, budget, seed, counts, plan->row_ptr, plan->col_idx,
+    e = abatt::launch_sampler(s, S, budget, seed, ws + l.sampler, plan->row_ptr, plan->col_idx,
                               plan->logw, plan->capacity, plan->status, stream);
   return hip_status(e);
 }

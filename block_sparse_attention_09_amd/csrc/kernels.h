@@ -19,19 +19,26 @@ struct Shape {
   bool bf16;     // dtype of Q/K/V/O
 };
 
-// key_means.hip
+// key_means.hip: fp32 means [B,H,n_kbs,D], or the same means as two bf16
+// planes (hi then lo, each [B,H,n_kbs,D]) for the scoring MFMAs
 hipError_t launch_key_means(const Shape& s, const void* K, float* kmean, hipStream_t st);
+hipError_t launch_key_means_split(const Shape& s, const void* K, uint16_t* planes, hipStream_t st);
 
 // kmeans.hip: centroids [R, C, D] fp32 and weights [R, C] fp32
 hipError_t launch_kmeans(const Shape& s, const void* Q, float* mu, float* w, hipStream_t st);
 
-// score.hip: S [R, n_kbs] fp32 from centroids, weights and key means
-hipError_t launch_scores(const Shape& s, const float* mu, const float* w, const float* kmean,
+// score.hip: S [R, n_kbs] fp32 from centroids, weights and the split key means
+hipError_t launch_scores(const Shape& s, const float* mu, const float* w, const uint16_t* kplanes,
                          float* S, hipStream_t st);
 
-// sampler.hip: counts -> row_ptr -> col_idx/logw
+// sampler.hip: counts -> row_ptr -> col_idx/logw.  The sampler's scratch
+// (row counts, kept-block bitmasks, per-row solves) lives in `ws`.
+struct SamplerWs {
+  size_t counts, masks, solves, total;
+};
+SamplerWs sampler_ws_layout(const Shape& s);
 hipError_t launch_sampler(const Shape& s, const float* S, double budget, uint64_t seed,
-                          int32_t* counts, int32_t* row_ptr, int32_t* col_idx, float* logw,
+                          void* ws, int32_t* row_ptr, int32_t* col_idx, float* logw,
                           int64_t capacity, int32_t* status, hipStream_t st);
 
 // attend.hip: gathered (plan != null) or dense attention

@@ -10,8 +10,11 @@
 
 namespace abatt {
 
-// bf16 input: one thread = 8 dims of one block (4 x 16-byte loads).
-template <int D>
+// bf16 input: one thread = 8 dims of one block (4 x 16-byte loads).  Writes
+// either the fp32 means or (kSplit) the means as two bf16 planes hi + lo with
+// hi = bf16(mean), lo = bf16(mean - hi): the operands of the split-bf16
+// scoring MFMAs, which then stage them without any conversion.
+template <int D, bool kSplit>
 __global__ __launch_bounds__(256) void k_key_means_bf16(const uint16_t* __restrict__ K,
                                                         float* __restrict__ kmean,
                                                         int64_t total, int N, int n_kbs) {
@@ -37,14 +40,30 @@ __global__ __launch_bounds__(256) void k_key_means_bf16(const uint16_t* __restri
       out[2 * e] = (((a0 + a1) + a2) + a3) * 0.25f;
       out[2 * e + 1] = (((b0 + b1) + b2) + b3) * 0.25f;
     }
-    float* dst = kmean + bj * D + 8 * c;
-    *reinterpret_cast<f32x4*>(dst) = f32x4{out[0], out[1], out[2], out[3]};
-    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{out[4], out[5], out[6], out[7]};
+    if constexpr (kSplit) {
+      uint16_t* hi = reinterpret_cast<uint16_t*>(kmean);
+      uint16_t* lo = hi + total * 8;
+      u32x4 h, l;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t h0 = f32_to_bf16_bits(out[2 * e]), h1 = f32_to_bf16_bits(out[2 * e + 1]);
+        const uint32_t l0 = f32_to_bf16_bits(out[2 * e] - bf16_bits_to_f32(h0));
+        const uint32_t l1 = f32_to_bf16_bits(out[2 * e + 1] - bf16_bits_to_f32(h1));
+        h[e] = h0 | (h1 << 16);
+        l[e] = l0 | (l1 << 16);
+      }
+      *reinterpret_cast<u32x4*>(hi + bj * D + 8 * c) = h;
+      *reinterpret_cast<u32x4*>(lo + bj * D + 8 * c) = l;
+    } else {
+      float* dst = kmean + bj * D + 8 * c;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{out[0], out[1], out[2], out[3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{out[4], out[5], out[6], out[7]};
+    }
   }
 }
 
-// fp32 input: one thread = 4 dims of one block.
-template <int D>
+// fp32 input: one thread = 4 dims of one block (same two output forms).
+template <int D, bool kSplit>
 __global__ __launch_bounds__(256) void k_key_means_f32(const float* __restrict__ K,
                                                        float* __restrict__ kmean,
                                                        int64_t total, int N, int n_kbs) {
@@ -63,27 +82,49 @@ __global__ __launch_bounds__(256) void k_key_means_f32(const float* __restrict__
     f32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = (((r0[e] + r1[e]) + r2[e]) + r3[e]) * 0.25f;
-    *reinterpret_cast<f32x4*>(kmean + bj * D + 4 * c) = o;
+    if constexpr (kSplit) {
+      uint16_t* hi = reinterpret_cast<uint16_t*>(kmean);
+      uint16_t* lo = hi + total * 4;
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = f32_to_bf16_bits(o[e]);
+        l[e] = f32_to_bf16_bits(o[e] - bf16_bits_to_f32(h[e]));
+      }
+      *reinterpret_cast<u32x2*>(hi + bj * D + 4 * c) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      *reinterpret_cast<u32x2*>(lo + bj * D + 4 * c) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+    } else {
+      *reinterpret_cast<f32x4*>(kmean + bj * D + 4 * c) = o;
+    }
   }
 }
 
-hipError_t launch_key_means(const Shape& s, const void* K, float* kmean, hipStream_t st) {
+template <bool kSplit>
+static hipError_t launch_means(const Shape& s, const void* K, float* out, hipStream_t st) {
   const int64_t blocks = (int64_t)s.B * s.H * s.n_kbs;
   const int64_t total = blocks * (s.bf16 ? s.D / 8 : s.D / 4);
   const int64_t want = (total + 255) / 256;
   const int grid = (int)(want < 65536 ? want : 65536);
   if (s.bf16) {
     if (s.D == 128)
-      k_key_means_bf16<128><<<grid, 256, 0, st>>>((const uint16_t*)K, kmean, total, s.N, s.n_kbs);
+      k_key_means_bf16<128, kSplit><<<grid, 256, 0, st>>>((const uint16_t*)K, out, total, s.N, s.n_kbs);
     else
-      k_key_means_bf16<64><<<grid, 256, 0, st>>>((const uint16_t*)K, kmean, total, s.N, s.n_kbs);
+      k_key_means_bf16<64, kSplit><<<grid, 256, 0, st>>>((const uint16_t*)K, out, total, s.N, s.n_kbs);
   } else {
     if (s.D == 128)
-      k_key_means_f32<128><<<grid, 256, 0, st>>>((const float*)K, kmean, total, s.N, s.n_kbs);
+      k_key_means_f32<128, kSplit><<<grid, 256, 0, st>>>((const float*)K, out, total, s.N, s.n_kbs);
     else
-      k_key_means_f32<64><<<grid, 256, 0, st>>>((const float*)K, kmean, total, s.N, s.n_kbs);
+      k_key_means_f32<64, kSplit><<<grid, 256, 0, st>>>((const float*)K, out, total, s.N, s.n_kbs);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_key_means(const Shape& s, const void* K, float* kmean, hipStream_t st) {
+  return launch_means<false>(s, K, kmean, st);
+}
+
+hipError_t launch_key_means_split(const Shape& s, const void* K, uint16_t* planes, hipStream_t st) {
+  return launch_means<true>(s, K, reinterpret_cast<float*>(planes), st);
 }
 
 }  // namespace abatt

@@ -16,11 +16,13 @@
 //     so every run gives the same bits.
 //   * draws: block j uses word j%4 of Philox4x64-10(counter (j/4, qb, h, b),
 //     key (seed, 0)); kept iff its top 53 bits < pi_j * 2^53 (exact compare).
-// k_sip_count writes the row's kept count; k_scan turns counts into row_ptr
-// (and flags a plan that exceeds its capacity); k_sip_fill repeats the same
-// deterministic solve and draws and writes ascending block ids and
-// logw = -ln(pi) (float64 log, rounded to fp32; 0 where pi = 1).  Forced
-// (text) blocks follow the sampled ones with logw 0.
+// k_sip_count solves pi, draws, and records the row's kept-block bitmask, its
+// count and its solve (mode, c, theta); k_scan turns counts into row_ptr (and
+// flags a plan that exceeds its capacity); k_sip_fill walks the bitmask and
+// writes ascending block ids with logw = -ln(pi) (float64 log, rounded to
+// fp32; 0 where pi = 1), re-deriving pi of each kept block from its score and
+// the recorded solve.  Forced (text) blocks follow the sampled ones with
+// logw 0.
 #include "common.h"
 #include "kernels.h"
 
@@ -47,7 +49,7 @@ __device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64
   }
 }
 
-constexpr int kSampT = 256;
+constexpr int kSampT = 512;
 constexpr int kSampWaves = kSampT / 64;
 constexpr double kTwo53 = 9007199254740992.0;
 
@@ -94,10 +96,11 @@ __device__ __forceinline__ int block_sum_i32(int v, Red& red) {
 }
 
 struct PiSolve {
-  int mode;      // 0: every block pi=1; 1: pi=1 on positive scores; 2: capped-proportional
   double c;      // proportionality constant (mode 2)
   float theta;   // certain iff s >= theta (mode 2)
+  int mode;      // 0: every block pi=1; 1: pi=1 on positive scores; 2: capped-proportional
 };
+static_assert(sizeof(PiSolve) == 16, "row solve record is 16 bytes");
 
 __device__ __forceinline__ double pi_of(float s, const PiSolve& ps) {
   if (ps.mode == 0) return 1.0;
@@ -185,7 +188,9 @@ template <bool kLds>
 __global__ __launch_bounds__(kSampT) void k_sip_count(const float* __restrict__ S, int n,
                                                      int n_forced, int n_qb, int H,
                                                      double budget, uint64_t seed,
-                                                     int32_t* __restrict__ counts) {
+                                                     int32_t* __restrict__ counts,
+                                                     uint32_t* __restrict__ masks,
+                                                     PiSolve* __restrict__ solves) {
   extern __shared__ __align__(16) float srow[];
   __shared__ Red red;
   const int r = blockIdx.x;
@@ -193,11 +198,26 @@ __global__ __launch_bounds__(kSampT) void k_sip_count(const float* __restrict__ 
   const float* s = stage_row<kLds>(S + (int64_t)r * n, n, srow);
   const PiSolve ps = solve_pi(s, n, budget, red);
   const int groups = (n + 3) / 4;
+  const int words = (n + 31) / 32;
+  uint32_t* mrow = masks + (int64_t)r * words;
+  const int t = threadIdx.x;
   int cnt = 0;
-  for (int g = threadIdx.x; g < groups; g += kSampT)
-    cnt += __popc(draw_group(s, n, g, qb, h, b, seed, ps));
+  for (int base = 0; base < 8 * words; base += kSampT) {
+    const int g = base + t;
+    const uint32_t nib = g < groups ? draw_group(s, n, g, qb, h, b, seed, ps) : 0u;
+    cnt += __popc(nib);
+    // eight consecutive groups (threads) make one 32-bit mask word
+    uint32_t wv = nib << (4 * (t & 7));
+    wv |= __shfl_xor(wv, 1);
+    wv |= __shfl_xor(wv, 2);
+    wv |= __shfl_xor(wv, 4);
+    if ((t & 7) == 0 && g / 8 < words) mrow[g / 8] = wv;
+  }
   cnt = block_sum_i32(cnt, red);
-  if (threadIdx.x == 0) counts[r] = cnt + n_forced;
+  if (t == 0) {
+    counts[r] = cnt + n_forced;
+    solves[r] = ps;
+  }
 }
 
 // Exclusive scan of the row counts -> row_ptr (single work-group).
@@ -236,30 +256,28 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ count
   }
 }
 
-template <bool kLds>
 __global__ __launch_bounds__(kSampT) void k_sip_fill(const float* __restrict__ S, int n,
-                                                    int n_forced, int n_qb, int H,
-                                                    double budget, uint64_t seed,
+                                                    int n_forced,
+                                                    const uint32_t* __restrict__ masks,
+                                                    const PiSolve* __restrict__ solves,
                                                     const int32_t* __restrict__ row_ptr,
                                                     const int32_t* __restrict__ status,
                                                     int32_t* __restrict__ col_idx,
                                                     float* __restrict__ logw) {
-  extern __shared__ __align__(16) float srow[];
-  __shared__ Red red;
   __shared__ int wtot[kSampWaves];
   if (*status != 0) return;  // plan exceeded its capacity: nothing is written
   const int r = blockIdx.x;
-  const int qb = r % n_qb, bh = r / n_qb, h = bh % H, b = bh / H;
-  const float* s = stage_row<kLds>(S + (int64_t)r * n, n, srow);
-  const PiSolve ps = solve_pi(s, n, budget, red);
+  const int words = (n + 31) / 32;
+  const uint32_t* mrow = masks + (int64_t)r * words;
+  const float* srow = S + (int64_t)r * n;
+  const PiSolve ps = solves[r];
   const int64_t start = row_ptr[r];
-  const int groups = (n + 3) / 4;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   int run = 0;
-  for (int base = 0; base < groups; base += kSampT) {
-    const int g = base + t;
-    const uint32_t mask = g < groups ? draw_group(s, n, g, qb, h, b, seed, ps) : 0u;
-    const int k = __popc(mask);
+  for (int base = 0; base < words; base += kSampT) {
+    const int wi = base + t;
+    const uint32_t m = wi < words ? mrow[wi] : 0u;
+    const int k = __popc(m);
     int incl = k;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -275,15 +293,15 @@ __global__ __launch_bounds__(kSampT) void k_sip_fill(const float* __restrict__ S
       tot += wtot[q];
     }
     int64_t pos = start + run + before + incl - k;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (mask & (1u << i)) {
-        const int j = 4 * g + i;
-        const double pi = pi_of(s[j], ps);
-        col_idx[pos] = j;
-        logw[pos] = pi == 1.0 ? 0.0f : (float)(-log(pi));
-        ++pos;
-      }
+    uint32_t mm = m;
+    while (mm) {
+      const int bit = __ffs(mm) - 1;
+      mm &= mm - 1;
+      const int j = 32 * wi + bit;
+      const double pi = pi_of(srow[j], ps);
+      col_idx[pos] = j;
+      logw[pos] = pi == 1.0 ? 0.0f : (float)(-log(pi));
+      ++pos;
     }
     run += tot;
     __syncthreads();
@@ -298,38 +316,49 @@ constexpr size_t kSampLdsMax = 150 * 1024;
 
 template <bool kLds>
 static hipError_t launch_sampler_t(const Shape& s, const float* S, double budget, uint64_t seed,
-                                   int32_t* counts, int32_t* row_ptr, int32_t* col_idx,
-                                   float* logw, int64_t capacity, int32_t* status,
-                                   hipStream_t st) {
+                                   void* ws, int32_t* row_ptr, int32_t* col_idx, float* logw,
+                                   int64_t capacity, int32_t* status, hipStream_t st) {
   const size_t lds = kLds ? (size_t)s.n_kbs * sizeof(float) : 0;
   const int n_forced = s.n_kb - s.n_kbs;
+  SamplerWs l = sampler_ws_layout(s);
+  char* base = static_cast<char*>(ws);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + l.counts);
+  uint32_t* masks = reinterpret_cast<uint32_t*>(base + l.masks);
+  PiSolve* solves = reinterpret_cast<PiSolve*>(base + l.solves);
   if (kLds) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_sip_count<kLds>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_sip_fill<kLds>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
   }
   k_sip_count<kLds><<<s.R, kSampT, lds, st>>>(S, s.n_kbs, n_forced, s.n_qb, s.H, budget, seed,
-                                              counts);
+                                              counts, masks, solves);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   k_scan<<<1, 1024, 0, st>>>(counts, s.R, row_ptr, capacity, status);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_sip_fill<kLds><<<s.R, kSampT, lds, st>>>(S, s.n_kbs, n_forced, s.n_qb, s.H, budget, seed,
-                                             row_ptr, status, col_idx, logw);
+  k_sip_fill<<<s.R, kSampT, 0, st>>>(S, s.n_kbs, n_forced, masks, solves, row_ptr, status,
+                                     col_idx, logw);
   return hipGetLastError();
 }
 
+SamplerWs sampler_ws_layout(const Shape& s) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  SamplerWs l;
+  l.counts = 0;
+  l.masks = up((size_t)s.R * sizeof(int32_t));
+  l.solves = l.masks + up((size_t)s.R * ((s.n_kbs + 31) / 32) * sizeof(uint32_t));
+  l.total = l.solves + up((size_t)s.R * sizeof(PiSolve));
+  return l;
+}
+
 hipError_t launch_sampler(const Shape& s, const float* S, double budget, uint64_t seed,
-                          int32_t* counts, int32_t* row_ptr, int32_t* col_idx, float* logw,
+                          void* ws, int32_t* row_ptr, int32_t* col_idx, float* logw,
                           int64_t capacity, int32_t* status, hipStream_t st) {
   if ((size_t)s.n_kbs * sizeof(float) <= kSampLdsMax)
-    return launch_sampler_t<true>(s, S, budget, seed, counts, row_ptr, col_idx, logw, capacity,
+    return launch_sampler_t<true>(s, S, budget, seed, ws, row_ptr, col_idx, logw, capacity,
                                   status, st);
-  return launch_sampler_t<false>(s, S, budget, seed, counts, row_ptr, col_idx, logw, capacity,
+  return launch_sampler_t<false>(s, S, budget, seed, ws, row_ptr, col_idx, logw, capacity,
                                  status, st);
 }
 

@@ -7,7 +7,8 @@
 //   s_j = sum_c w_c * softmax_j(scale * mu_c . kmean_j),   j over sparse blocks.
 //
 // One work-group holds 128 centroid rows (128/C query blocks of one head) and
-// streams that head's key means twice, 32 blocks per tile, through LDS:
+// streams that head's key means twice, 32 blocks per tile, through LDS (the
+// means arrive as bf16 hi and lo planes written by the key-means kernel):
 //   pass 1: per-centroid running max and sum of exp2 (the softmax normaliser);
 //   pass 2: p = exp2(logit + log2 w_c - lse_c), summed over the C centroids of
 //           each query block and written to S.
@@ -23,23 +24,18 @@
 
 namespace abatt {
 
-template <int D>
-struct ScoreTile {
-  static constexpr int ROWB = D + 8;            // LDS row stride (bf16 elements)
-  static constexpr int NREG = D / 32;           // float4 staging loads per thread
-};
-
 template <int D, int C>
 __global__ __launch_bounds__(256, 2) void k_scores(const float* __restrict__ mu,
                                                    const float* __restrict__ w,
-                                                   const float* __restrict__ kmean,
+                                                   const uint16_t* __restrict__ kplanes,
                                                    float* __restrict__ S, int n_qb, int n_kbs,
                                                    int groups_per_head, int n_groups,
-                                                   float scale_log2) {
+                                                   int64_t plane_elems, float scale_log2) {
   constexpr int G = 128 / C;      // query blocks per work-group
   constexpr int KS = D / 16;      // MFMA k-steps
-  constexpr int ROWB = ScoreTile<D>::ROWB;
-  constexpr int NREG = ScoreTile<D>::NREG;
+  constexpr int ROWB = D + 8;     // LDS row stride (bf16), padded: conflict-free operand reads
+  constexpr int CH = D / 8;       // 16-byte chunks per key-mean row
+  constexpr int NCH = CH / 8;     // chunks per thread per plane per 32-key tile
   __shared__ __align__(16) uint16_t khi[2][32 * ROWB];
   __shared__ __align__(16) uint16_t klo[2][32 * ROWB];
   __shared__ float a_lds[128];
@@ -75,46 +71,52 @@ __global__ __launch_bounds__(256, 2) void k_scores(const float* __restrict__ mu,
   }
   const float wc = rvalid ? w[prow * C + cc] : 0.f;
 
-  const float* kbase = kmean + (int64_t)bh * n_kbs * D;
+  const uint16_t* hbase = kplanes + (int64_t)bh * n_kbs * D;
+  const uint16_t* lbase = hbase + plane_elems;
   const int n_tiles = (n_kbs + 31) / 32;
-  f32x4 reg[NREG];
+  const int tlast = n_tiles - 1;
+  u32x4 rh[NCH], rl[NCH];
 
+  // Tile pipeline (as in the attention kernel): tile t is computed from LDS
+  // stage t%2 while the registers carry tile t+1; at the top of iteration t
+  // the registers go to the free stage and the loads of tile t+2 are issued.
   auto load_tile = [&](int tile) {
 #pragma unroll
-    for (int i = 0; i < NREG; ++i) {
-      const int idx = (i * 256 + t) * 4;
-      const int key = 32 * tile + idx / D, e = idx % D;
-      reg[i] = key < n_kbs ? *reinterpret_cast<const f32x4*>(kbase + (int64_t)key * D + e)
-                           : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NCH; ++i) {
+      const int q = i * 256 + t;
+      int key = 32 * tile + q / CH;
+      key = key < n_kbs ? key : n_kbs - 1;  // rows past the end are masked later
+      const int64_t off = (int64_t)key * D + 8 * (q % CH);
+      rh[i] = *reinterpret_cast<const u32x4*>(hbase + off);
+      rl[i] = *reinterpret_cast<const u32x4*>(lbase + off);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < NREG; ++i) {
-      const int idx = (i * 256 + t) * 4;
-      const int key = idx / D, e = idx % D;
-      uint32_t h[4], l[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        h[q] = f32_to_bf16_bits(reg[i][q]);
-        l[q] = f32_to_bf16_bits(reg[i][q] - bf16_bits_to_f32(h[q]));
-      }
-      *reinterpret_cast<u32x2*>(&khi[buf][key * ROWB + e]) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-      *reinterpret_cast<u32x2*>(&klo[buf][key * ROWB + e]) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+    for (int i = 0; i < NCH; ++i) {
+      const int q = i * 256 + t;
+      const int o = (q / CH) * ROWB + 8 * (q % CH);
+      *reinterpret_cast<u32x4*>(&khi[buf][o]) = rh[i];
+      *reinterpret_cast<u32x4*>(&klo[buf][o]) = rl[i];
     }
   };
   auto kop = [&](const uint16_t* base, int s) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(base + l32 * ROWB + 16 * s + 8 * hh);
   };
+  auto prologue = [&]() {
+    load_tile(0);
+    store_tile(0);
+    load_tile(n_tiles > 1 ? 1 : 0);
+    __syncthreads();
+  };
 
   // ---------------- pass 1: softmax normaliser of every centroid ----------------
   float m_run = -INFINITY, s_run = 0.f;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  prologue();
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int buf = tile & 1;
-    if (tile + 1 < n_tiles) load_tile(tile + 1);
+    store_tile(buf ^ 1);
+    load_tile(min(tile + 2, tlast));
     f32x16 big = {}, small = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -139,7 +141,6 @@ __global__ __launch_bounds__(256, 2) void k_scores(const float* __restrict__ mu,
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v) s_run += __builtin_amdgcn_exp2f(x[v] - m_run);
-    if (tile + 1 < n_tiles) store_tile(buf ^ 1);
     __syncthreads();
   }
   s_run += __shfl_xor(s_run, 32);
@@ -153,12 +154,11 @@ __global__ __launch_bounds__(256, 2) void k_scores(const float* __restrict__ mu,
 #pragma unroll
   for (int v = 0; v < 16; ++v) a_v[v] = a_lds[32 * wv + 8 * (v >> 2) + 4 * hh + (v & 3)];
   float* srow_base = S + ((int64_t)bh * n_qb) * n_kbs;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  prologue();
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int buf = tile & 1;
-    if (tile + 1 < n_tiles) load_tile(tile + 1);
+    store_tile(buf ^ 1);
+    load_tile(min(tile + 2, tlast));
     f32x16 big = {}, small = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -199,29 +199,29 @@ __global__ __launch_bounds__(256, 2) void k_scores(const float* __restrict__ mu,
       const int q = qb0 + 2 * wv + hh;
       if (q < n_qb && key < n_kbs) srow_base[(int64_t)q * n_kbs + key] = tot[hh];
     }
-    if (tile + 1 < n_tiles) store_tile(buf ^ 1);
     __syncthreads();
   }
 }
 
 template <int D, int C>
 static hipError_t launch_scores_t(const Shape& s, const float* mu, const float* w,
-                                  const float* kmean, float* S, hipStream_t st) {
+                                  const uint16_t* kplanes, float* S, hipStream_t st) {
   constexpr int G = 128 / C;
   const int gph = (s.n_qb + G - 1) / G;
   const int n_groups = s.B * s.H * gph;
-  k_scores<D, C><<<n_groups, 256, 0, st>>>(mu, w, kmean, S, s.n_qb, s.n_kbs, gph, n_groups,
-                                           s.scale * kLog2e);
+  const int64_t plane = (int64_t)s.B * s.H * s.n_kbs * s.D;
+  k_scores<D, C><<<n_groups, 256, 0, st>>>(mu, w, kplanes, S, s.n_qb, s.n_kbs, gph, n_groups,
+                                           plane, s.scale * kLog2e);
   return hipGetLastError();
 }
 
-hipError_t launch_scores(const Shape& s, const float* mu, const float* w, const float* kmean,
+hipError_t launch_scores(const Shape& s, const float* mu, const float* w, const uint16_t* kplanes,
                          float* S, hipStream_t st) {
   if (s.D == 128)
-    return s.n_clusters == 8 ? launch_scores_t<128, 8>(s, mu, w, kmean, S, st)
-                             : launch_scores_t<128, 16>(s, mu, w, kmean, S, st);
-  return s.n_clusters == 8 ? launch_scores_t<64, 8>(s, mu, w, kmean, S, st)
-                           : launch_scores_t<64, 16>(s, mu, w, kmean, S, st);
+    return s.n_clusters == 8 ? launch_scores_t<128, 8>(s, mu, w, kplanes, S, st)
+                             : launch_scores_t<128, 16>(s, mu, w, kplanes, S, st);
+  return s.n_clusters == 8 ? launch_scores_t<64, 8>(s, mu, w, kplanes, S, st)
+                           : launch_scores_t<64, 16>(s, mu, w, kplanes, S, st);
 }
 
 }  // namespace abatt
