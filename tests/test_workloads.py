@@ -77,3 +77,12 @@ def test_drift_sequence():
 
 
 TINY_DIGEST = "aad07a999b1474c410aae359c3bb962103daffb1660dbf0111653148a6aa574a"
+
+
+def test_drift_subset_matches_full_layer():
+    wl = Workload("t", B=1, H=3, D=64, grid=(1, 4, 8), drift=0.05, plan_reuse=3)
+    full = make_qkv_sequence(wl, 3)
+    sub = make_qkv_sequence(wl, 3, heads=1)
+    for c in range(3):
+        np.testing.assert_array_equal(sub[c][0][0, 0], full[c][0][0, 0])
+        np.testing.assert_array_equal(sub[c][1][0, 0], full[c][1][0, 0])

@@ -184,12 +184,8 @@ def make_qkv(wl: Workload, heads: Optional[int] = None
     v = np.empty_like(q)
     gen = Generator(wl)
     for b, h, qh, kh, vh in gen.iter_heads():
-        if b >= B:
-            break
-        if h >= H:
-            if heads is not None:
-                break
-            continue
+        if b >= B or h >= H:
+            break                       # heads come in order: the subset is done
         q[b, h] = round_like(qh, wl.dtype)
         k[b, h] = round_like(kh, wl.dtype)
         v[b, h] = round_like(vh, wl.dtype)
@@ -215,12 +211,18 @@ def make_qkv_sequence(wl: Workload, calls: int, heads: Optional[int] = None
             qm[b, h], km[b, h], vm[b, h] = qh, kh, vh
     out = []
     v = round_like(vm, wl.dtype)
+    shape = (wl.N, wl.D)
     for c in range(calls):
         if c > 0:
-            for b in range(B):
-                for h in range(H):
-                    qm[b, h] = gen.drift(qm[b, h])
-                    km[b, h] = gen.drift(km[b, h])
+            # draws for every head in order (so a subset matches the full layer)
+            for b in range(wl.B):
+                for h in range(wl.H):
+                    if b < B and h < H:
+                        qm[b, h] = gen.drift(qm[b, h])
+                        km[b, h] = gen.drift(km[b, h])
+                    else:
+                        gen.drift(np.zeros(shape, dtype=np.float32))
+                        gen.drift(np.zeros(shape, dtype=np.float32))
         out.append((round_like(qm, wl.dtype), round_like(km, wl.dtype), v))
     return out
 
