@@ -6,7 +6,7 @@
 // of the block's centroids to its averaged keys.
 //   s_j = sum_c w_c * softmax_j(scale * mu_c . kmean_j),   j over sparse blocks.
 //
-// One work-group holds 128 centroid rows (128/C query blocks of one head) and
+// One work-group holds 256 centroid rows (256/C query blocks of one head) and
 // streams that head's key means twice, 32 blocks per tile, through LDS (the
 // means arrive as bf16 hi and lo planes written by the key-means kernel):
 //   pass 1: per-centroid running max and sum of exp2 (the softmax normaliser);
@@ -24,21 +24,27 @@
 
 namespace abatt {
 
+constexpr int kScoreWaves = 8;                 // 256 centroid rows per work-group
+constexpr int kScoreT = 64 * kScoreWaves;
+constexpr int kScoreStages = 3;                // LDS ring of key-mean tiles
+
 template <int D, int C>
-__global__ __launch_bounds__(256, 2) void k_scores(const float* __restrict__ mu,
-                                                   const float* __restrict__ w,
-                                                   const uint16_t* __restrict__ kplanes,
-                                                   float* __restrict__ S, int n_qb, int n_kbs,
-                                                   int groups_per_head, int n_groups,
-                                                   int64_t plane_elems, float scale_log2) {
-  constexpr int G = 128 / C;      // query blocks per work-group
-  constexpr int KS = D / 16;      // MFMA k-steps
-  constexpr int ROWB = D + 8;     // LDS row stride (bf16), padded: conflict-free operand reads
-  constexpr int CH = D / 8;       // 16-byte chunks per key-mean row
-  constexpr int NCH = CH / 8;     // chunks per thread per plane per 32-key tile
-  __shared__ __align__(16) uint16_t khi[2][32 * ROWB];
-  __shared__ __align__(16) uint16_t klo[2][32 * ROWB];
-  __shared__ float a_lds[128];
+__global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__ mu,
+                                                       const float* __restrict__ w,
+                                                       const uint16_t* __restrict__ kplanes,
+                                                       float* __restrict__ S, int n_qb, int n_kbs,
+                                                       int groups_per_head, int n_groups,
+                                                       int64_t plane_elems, float scale_log2) {
+  constexpr int ROWS = 32 * kScoreWaves;  // centroid rows per work-group
+  constexpr int G = ROWS / C;             // query blocks per work-group
+  constexpr int KS = D / 16;              // MFMA k-steps
+  constexpr int ROWB = D + 8;             // LDS row stride (bf16), padded: conflict-free reads
+  constexpr int CH = D / 8;               // 16-byte chunks per key-mean row
+  constexpr int TILE_CH = 32 * CH;        // chunks per plane per 32-key tile
+  constexpr int NCH = (TILE_CH + kScoreT - 1) / kScoreT;  // per thread per plane
+  __shared__ __align__(16) uint16_t khi[kScoreStages][32 * ROWB];
+  __shared__ __align__(16) uint16_t klo[kScoreStages][32 * ROWB];
+  __shared__ float a_lds[ROWS];
 
   const int gid = xcd_remap(blockIdx.x, n_groups);
   const int bh = gid / groups_per_head;
@@ -75,65 +81,94 @@ __global__ __launch_bounds__(256, 2) void k_scores(const float* __restrict__ mu,
   const uint16_t* lbase = hbase + plane_elems;
   const int n_tiles = (n_kbs + 31) / 32;
   const int tlast = n_tiles - 1;
-  u32x4 rh[NCH], rl[NCH];
 
-  // Tile pipeline (as in the attention kernel): tile t is computed from LDS
-  // stage t%2 while the registers carry tile t+1; at the top of iteration t
-  // the registers go to the free stage and the loads of tile t+2 are issued.
-  auto load_tile = [&](int tile) {
+  // Tile pipeline: tile t is computed from LDS stage t%3.  Two register sets
+  // alternate (the loop is unrolled by two so they stay in registers): at the
+  // top of iteration t the set holding tile t+2 goes to stage (t+2)%3 (last
+  // read in iteration t-1, which ended with a barrier) and the same set is
+  // reloaded with tile t+4, so every load has two iterations to land.
+  struct Regs {
+    u32x4 h[NCH], l[NCH];
+  };
+  Regs ra, rb;
+  auto load_tile = [&](Regs& r, int tile) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int q = i * 256 + t;
+      const int q = i * kScoreT + t;
       int key = 32 * tile + q / CH;
       key = key < n_kbs ? key : n_kbs - 1;  // rows past the end are masked later
       const int64_t off = (int64_t)key * D + 8 * (q % CH);
-      rh[i] = *reinterpret_cast<const u32x4*>(hbase + off);
-      rl[i] = *reinterpret_cast<const u32x4*>(lbase + off);
+      if (q < TILE_CH) {
+        r.h[i] = *reinterpret_cast<const u32x4*>(hbase + off);
+        r.l[i] = *reinterpret_cast<const u32x4*>(lbase + off);
+      }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](const Regs& r, int stage) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int q = i * 256 + t;
-      const int o = (q / CH) * ROWB + 8 * (q % CH);
-      *reinterpret_cast<u32x4*>(&khi[buf][o]) = rh[i];
-      *reinterpret_cast<u32x4*>(&klo[buf][o]) = rl[i];
+      const int q = i * kScoreT + t;
+      if (q < TILE_CH) {
+        const int o = (q / CH) * ROWB + 8 * (q % CH);
+        *reinterpret_cast<u32x4*>(&khi[stage][o]) = r.h[i];
+        *reinterpret_cast<u32x4*>(&klo[stage][o]) = r.l[i];
+      }
     }
   };
   auto kop = [&](const uint16_t* base, int s) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(base + l32 * ROWB + 16 * s + 8 * hh);
   };
   auto prologue = [&]() {
-    load_tile(0);
-    store_tile(0);
-    load_tile(n_tiles > 1 ? 1 : 0);
+    load_tile(ra, 0);
+    store_tile(ra, 0);
+    load_tile(rb, min(1, tlast));
+    store_tile(rb, 1 % kScoreStages);
+    load_tile(ra, min(2, tlast));
+    load_tile(rb, min(3, tlast));
     __syncthreads();
+  };
+  // one pipelined pass; `body(tile, stage)` computes a tile
+  auto run_pass = [&](auto&& body) {
+    prologue();
+    int stage = 0;
+    for (int tile = 0; tile < n_tiles; tile += 2) {
+      store_tile(ra, (stage + 2) % kScoreStages);
+      load_tile(ra, min(tile + 4, tlast));
+      body(tile, stage);
+      __syncthreads();
+      stage = (stage + 1) % kScoreStages;
+      if (tile + 1 < n_tiles) {
+        store_tile(rb, (stage + 2) % kScoreStages);
+        load_tile(rb, min(tile + 5, tlast));
+        body(tile + 1, stage);
+        __syncthreads();
+        stage = (stage + 1) % kScoreStages;
+      }
+    }
   };
 
   // ---------------- pass 1: softmax normaliser of every centroid ----------------
   float m_run = -INFINITY, s_run = 0.f;
-  prologue();
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    store_tile(buf ^ 1);
-    load_tile(min(tile + 2, tlast));
-    f32x16 big = {}, small = {};
+  run_pass([&](int tile, int stage) {
+    // one accumulation chain: the small cross terms first, then hi*hi
+    f32x16 x = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const bf16x8 kh = kop(khi[buf], s), kl = kop(klo[buf], s);
-      small = mfma_bf16_32x32x16(kl, mh[s], small);
-      small = mfma_bf16_32x32x16(kh, ml[s], small);
-      big = mfma_bf16_32x32x16(kh, mh[s], big);
+      const bf16x8 kh = kop(khi[stage], s), kl = kop(klo[stage], s);
+      x = mfma_bf16_32x32x16(kl, mh[s], x);
+      x = mfma_bf16_32x32x16(kh, ml[s], x);
     }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) x = mfma_bf16_32x32x16(kop(khi[stage], s), mh[s], x);
     // lane: centroid l32, keys 32*tile + 8*(v/4) + 4*hh + v%4
-    float x[16];
+    if (32 * tile + 32 > n_kbs) {  // only the last tile has keys past the end
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (32 * tile + 8 * (v >> 2) + 4 * hh + (v & 3) >= n_kbs) x[v] = -INFINITY;
+    }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = 32 * tile + 8 * (v >> 2) + 4 * hh + (v & 3);
-      x[v] = key < n_kbs ? big[v] + small[v] : -INFINITY;
-      tmax = fmaxf(tmax, x[v]);
-    }
+    for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, x[v]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     if (tmax > m_run) {
       s_run *= __builtin_amdgcn_exp2f(m_run - tmax);
@@ -141,8 +176,7 @@ __global__ __launch_bounds__(256, 2) void k_scores(const float* __restrict__ mu,
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v) s_run += __builtin_amdgcn_exp2f(x[v] - m_run);
-    __syncthreads();
-  }
+  });
   s_run += __shfl_xor(s_run, 32);
   // log2 of (w_c / normaliser); -inf for an empty cluster
   const float a_c = log2f(wc) - (m_run + log2f(s_run));
@@ -154,23 +188,20 @@ __global__ __launch_bounds__(256, 2) void k_scores(const float* __restrict__ mu,
 #pragma unroll
   for (int v = 0; v < 16; ++v) a_v[v] = a_lds[32 * wv + 8 * (v >> 2) + 4 * hh + (v & 3)];
   float* srow_base = S + ((int64_t)bh * n_qb) * n_kbs;
-  prologue();
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    store_tile(buf ^ 1);
-    load_tile(min(tile + 2, tlast));
-    f32x16 big = {}, small = {};
+  run_pass([&](int tile, int stage) {
+    f32x16 x = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const bf16x8 kh = kop(khi[buf], s), kl = kop(klo[buf], s);
-      small = mfma_bf16_32x32x16(mh[s], kl, small);
-      small = mfma_bf16_32x32x16(ml[s], kh, small);
-      big = mfma_bf16_32x32x16(mh[s], kh, big);
+      const bf16x8 kh = kop(khi[stage], s), kl = kop(klo[stage], s);
+      x = mfma_bf16_32x32x16(mh[s], kl, x);
+      x = mfma_bf16_32x32x16(ml[s], kh, x);
     }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) x = mfma_bf16_32x32x16(mh[s], kop(khi[stage], s), x);
     // lane: key 32*tile + l32, centroid rows 32*wv + 8*(v/4) + 4*hh + v%4
     float p[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(big[v] + small[v] + a_v[v]);
+    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(x[v] + a_v[v]);
     const int key = 32 * tile + l32;
     if constexpr (C == 8) {
       // rows 8g..8g+7 of the wave = one query block; this half holds 4 of them
@@ -199,18 +230,17 @@ __global__ __launch_bounds__(256, 2) void k_scores(const float* __restrict__ mu,
       const int q = qb0 + 2 * wv + hh;
       if (q < n_qb && key < n_kbs) srow_base[(int64_t)q * n_kbs + key] = tot[hh];
     }
-    __syncthreads();
-  }
+  });
 }
 
 template <int D, int C>
 static hipError_t launch_scores_t(const Shape& s, const float* mu, const float* w,
                                   const uint16_t* kplanes, float* S, hipStream_t st) {
-  constexpr int G = 128 / C;
+  constexpr int G = 32 * kScoreWaves / C;
   const int gph = (s.n_qb + G - 1) / G;
   const int n_groups = s.B * s.H * gph;
   const int64_t plane = (int64_t)s.B * s.H * s.n_kbs * s.D;
-  k_scores<D, C><<<n_groups, 256, 0, st>>>(mu, w, kplanes, S, s.n_qb, s.n_kbs, gph, n_groups,
+  k_scores<D, C><<<n_groups, kScoreT, 0, st>>>(mu, w, kplanes, S, s.n_qb, s.n_kbs, gph, n_groups,
                                            plane, s.scale * kLog2e);
   return hipGetLastError();
 }
