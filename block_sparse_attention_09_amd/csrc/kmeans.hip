@@ -141,6 +141,212 @@ __global__ __launch_bounds__(256) void k_kmeans(const T* __restrict__ Q, float* 
   if (t < C) w_out[(int64_t)r * C + t] = (float)ccount[t] / (float)n;
 }
 
+// bf16 queries: the same Lloyd iterations with both contractions on the
+// matrix cores (v_mfma_f32_16x16x32_bf16).  Per iteration and block:
+//   dots[c][p] = mu_c . x_p  as a [16 x D] centroid tile times X^T, each
+//     centroid split into three bf16 planes (hi + mid + lo = its fp32 value),
+//     so the products are exact and the sums fp32 as in the scalar path; the
+//     queries are bf16 already;
+//   sums[e][c] = sum_p x_p[e] onehot[c][p]  (exact products, fp32 sums), and
+//     counts[c] from the same one-hot operand.
+// Wave w owns points 32w..32w+31 in the assignment and dims D/4*w.. in the
+// update; the query operands of both products are built once, in registers.
+// Lane layout of the 16x16 product: A row = B column = lane % 16 (k slots by
+// lane / 16), D[4*(lane/16) + v][lane % 16] in accumulator element v.  The
+// update thus leaves lane (g, i) with cluster i and 4 consecutive dims, which
+// it rounds to the planes with packed conversions and 8-byte writes.
+template <int D, int C>
+__global__ __launch_bounds__(256) void k_kmeans_mfma(const uint16_t* __restrict__ Q,
+                                                     float* __restrict__ mu_out,
+                                                     float* __restrict__ w_out, int N, int n_qb,
+                                                     int iters) {
+  constexpr int QB = 128;
+  constexpr int KS = D / 32;  // k steps of the distance product
+  constexpr int UT = D / 64;  // 16-dim update tiles per wave
+  constexpr int XS = D + 8;   // padded row of the staged queries / planes (bf16)
+  constexpr int OS = QB + 8;  // padded row of the one-hot matrix (bf16)
+  static_assert(C % 4 == 0 && C <= 16, "one 16-row centroid tile");
+  // the staged queries are only read while the operands are built; the
+  // centroid planes reuse their space afterwards
+  __shared__ __align__(16) uint16_t lds[QB * XS];
+  __shared__ __align__(16) uint16_t oh[16 * OS];  // onehot[c][p] of the last assignment
+  __shared__ __align__(16) float npart[4][16];    // per-wave partial |mu_c|^2
+  uint16_t* xs = lds;
+  uint16_t* planes = lds;  // [3][16][XS] after set-up
+
+  const int r = blockIdx.x;
+  const int qb = r % n_qb;
+  const int64_t bh = r / n_qb;
+  const int q0 = qb * QB;
+  const int n = min(QB, N - q0);
+  const int t = threadIdx.x;
+  const int w = t >> 6, l = t & 63, g = l >> 4, i = l & 15;
+
+  {  // stage the block's queries; rows past the end are zero
+    const u32x4* src = reinterpret_cast<const u32x4*>(Q + (bh * N + q0) * D);
+    constexpr int CH = D / 8;
+    for (int k = t; k < QB * CH; k += 256) {
+      const int row = k / CH, ch = k % CH;
+      const u32x4 v = row < n ? src[k] : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(xs + row * XS + 8 * ch) = v;
+    }
+  }
+  for (int k = t; k < 16 * OS / 2; k += 256) reinterpret_cast<uint32_t*>(oh)[k] = 0u;
+  __syncthreads();
+
+  // distance operand (B = X^T): point 32w + 16u + i, dims 32ks + 8g .. +7
+  bf16x8 xb[2][KS];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      xb[u][ks] = *reinterpret_cast<const bf16x8*>(xs + (32 * w + 16 * u + i) * XS + 32 * ks + 8 * g);
+  // update operand (A = X^T): dim D/4*w + 16u + i, points 32ks + 8g .. +7
+  bf16x8 ub[UT][4];
+#pragma unroll
+  for (int u = 0; u < UT; ++u)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint16_t* col = xs + (32 * ks + 8 * g) * XS + (D / 4) * w + 16 * u + i;
+      u32x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = (uint32_t)col[(2 * j) * XS] | ((uint32_t)col[(2 * j + 1) * XS] << 16);
+      ub[u][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  // centroids in registers: mreg[u][v] = mu[i][D/4*w + 16u + 4g + v]; the
+  // initial centroid c is query floor(c*n/C); rows c >= C stay zero
+  float mreg[UT][4];
+#pragma unroll
+  for (int u = 0; u < UT; ++u) {
+    const u32x2 x = i < C ? *reinterpret_cast<const u32x2*>(xs + ((i * n) / C) * XS + (D / 4) * w +
+                                                            16 * u + 4 * g)
+                          : u32x2{0u, 0u};
+    mreg[u][0] = bf16_bits_to_f32(x[0] & 0xffffu);
+    mreg[u][1] = bf16_bits_to_f32(x[0] >> 16);
+    mreg[u][2] = bf16_bits_to_f32(x[1] & 0xffffu);
+    mreg[u][3] = bf16_bits_to_f32(x[1] >> 16);
+  }
+  __syncthreads();
+
+  // centroids -> bf16 planes and per-wave partial squared norms
+  auto publish = [&]() {
+    float sq = 0.f;
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+      uint32_t hw[2], mw[2], lw[2];
+#pragma unroll
+      for (int v2 = 0; v2 < 2; ++v2) {
+        const f32x2 m = {mreg[u][2 * v2], mreg[u][2 * v2 + 1]};
+        const bf16x2 h = __builtin_convertvector(m, bf16x2);
+        const f32x2 r1 = m - __builtin_convertvector(h, f32x2);
+        const bf16x2 md = __builtin_convertvector(r1, bf16x2);
+        const bf16x2 lo = __builtin_convertvector(r1 - __builtin_convertvector(md, f32x2), bf16x2);
+        hw[v2] = __builtin_bit_cast(uint32_t, h);
+        mw[v2] = __builtin_bit_cast(uint32_t, md);
+        lw[v2] = __builtin_bit_cast(uint32_t, lo);
+        sq = fmaf(m[0], m[0], sq);
+        sq = fmaf(m[1], m[1], sq);
+      }
+      const int e = i * XS + (D / 4) * w + 16 * u + 4 * g;
+      *reinterpret_cast<u32x2*>(planes + e) = u32x2{hw[0], hw[1]};
+      *reinterpret_cast<u32x2*>(planes + 16 * XS + e) = u32x2{mw[0], mw[1]};
+      *reinterpret_cast<u32x2*>(planes + 32 * XS + e) = u32x2{lw[0], lw[1]};
+    }
+    sq += __shfl_xor(sq, 16);
+    sq += __shfl_xor(sq, 32);
+    if (g == 0) npart[w][i] = sq;
+  };
+  publish();
+  __syncthreads();
+
+  int cnt = 0;
+  for (int it = 0; it < iters; ++it) {
+    // assignment: nearest centroid by |mu_c|^2 - 2 x.mu_c; ties -> lower index
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(planes + pl * 16 * XS + i * XS + 32 * ks + 8 * g);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[u] = mfma_bf16_16x16x32(a, xb[u][ks], acc[u]);
+      }
+    }
+    f32x4 mn = *reinterpret_cast<const f32x4*>(&npart[0][4 * g]);
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) mn += *reinterpret_cast<const f32x4*>(&npart[ww][4 * g]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float best = 0.f;
+      int a = 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float d = 4 * g + v < C ? fmaf(-2.f, acc[u][v], mn[v]) : __builtin_inff();
+        if (v == 0 || d < best) {
+          best = d;
+          a = 4 * g + v;
+        }
+      }
+#pragma unroll
+      for (int o = 16; o < (C > 8 ? 64 : 32); o <<= 1) {
+        const float ob = __shfl_xor(best, o);
+        const int oa = __shfl_xor(a, o);
+        if (ob < best || (ob == best && oa < a)) {
+          best = ob;
+          a = oa;
+        }
+      }
+      // one-hot column of point p (rows c >= C and points p >= n stay zero)
+      const int p = 32 * w + 16 * u + i;
+      if (4 * g < C && p < n) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) oh[(4 * g + v) * OS + p] = a == 4 * g + v ? 0x3f80u : 0u;
+      }
+    }
+    __syncthreads();
+    // update: member sums on the matrix cores; counts from the one-hot bits
+    f32x4 sum[UT];
+#pragma unroll
+    for (int u = 0; u < UT; ++u) sum[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    cnt = 0;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 b = *reinterpret_cast<const u32x4*>(oh + i * OS + 32 * ks + 8 * g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cnt += __popc(b[j] & 0x00800080u);  // bit 7 of bf16 1.0
+      const bf16x8 B = __builtin_bit_cast(bf16x8, b);
+#pragma unroll
+      for (int u = 0; u < UT; ++u) sum[u] = mfma_bf16_16x16x32(ub[u][ks], B, sum[u]);
+    }
+    cnt += __shfl_xor(cnt, 16);
+    cnt += __shfl_xor(cnt, 32);  // members of cluster i
+    if (cnt > 0) {
+      // quotient sum / cnt: reciprocal estimate plus one residual correction
+      const float fc = (float)cnt;
+      const float inv = 1.f / fc;
+#pragma unroll
+      for (int u = 0; u < UT; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float q = sum[u][v] * inv;
+          mreg[u][v] = fmaf(fmaf(-q, fc, sum[u][v]), inv, q);
+        }
+    }
+    // every wave read this iteration's planes before the barrier above
+    publish();
+    __syncthreads();
+  }
+
+  if (i < C) {
+    float* mo = mu_out + ((int64_t)r * C + i) * D + (D / 4) * w + 4 * g;
+#pragma unroll
+    for (int u = 0; u < UT; ++u)
+      *reinterpret_cast<f32x4*>(mo + 16 * u) = f32x4{mreg[u][0], mreg[u][1], mreg[u][2], mreg[u][3]};
+    if (w == 0 && g == 0) w_out[(int64_t)r * C + i] = (float)cnt / (float)n;
+  }
+}
+
 template <typename T, int D, int C>
 static hipError_t launch_kmeans_t(const Shape& s, const void* Q, float* mu, float* w,
                                   hipStream_t st) {
@@ -160,10 +366,21 @@ static hipError_t launch_kmeans_d(const Shape& s, const void* Q, float* mu, floa
   return launch_kmeans_t<T, D, 16>(s, Q, mu, w, st);
 }
 
+template <int D, int C>
+static hipError_t launch_kmeans_mfma(const Shape& s, const void* Q, float* mu, float* w,
+                                     hipStream_t st) {
+  k_kmeans_mfma<D, C><<<s.R, 256, 0, st>>>((const uint16_t*)Q, mu, w, s.N, s.n_qb, s.kmeans_iters);
+  return hipGetLastError();
+}
+
 hipError_t launch_kmeans(const Shape& s, const void* Q, float* mu, float* w, hipStream_t st) {
-  if (s.bf16)
-    return s.D == 128 ? launch_kmeans_d<uint16_t, 128>(s, Q, mu, w, st)
-                      : launch_kmeans_d<uint16_t, 64>(s, Q, mu, w, st);
+  if (s.bf16) {
+    if (s.n_clusters == 8)
+      return s.D == 128 ? launch_kmeans_mfma<128, 8>(s, Q, mu, w, st)
+                        : launch_kmeans_mfma<64, 8>(s, Q, mu, w, st);
+    return s.D == 128 ? launch_kmeans_mfma<128, 16>(s, Q, mu, w, st)
+                      : launch_kmeans_mfma<64, 16>(s, Q, mu, w, st);
+  }
   return s.D == 128 ? launch_kmeans_d<float, 128>(s, Q, mu, w, st)
                     : launch_kmeans_d<float, 64>(s, Q, mu, w, st);
 }
