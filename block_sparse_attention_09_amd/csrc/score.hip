@@ -19,6 +19,10 @@
 // max), pass 2 uses the centroids as A (a lane holds 16 centroids of one key:
 // cheap sum over a query block's centroids).  The operand registers are the
 // same in both layouts.
+//
+// Each pass is software-pipelined: the MFMAs of tile t+1 are issued in the
+// same block as the exp2 work of tile t, so the matrix core and the vector
+// ALU run side by side.
 #include "common.h"
 #include "kernels.h"
 
@@ -38,12 +42,11 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
   constexpr int ROWS = 32 * kScoreWaves;  // centroid rows per work-group
   constexpr int G = ROWS / C;             // query blocks per work-group
   constexpr int KS = D / 16;              // MFMA k-steps
-  constexpr int ROWB = D + 8;             // LDS row stride (bf16), padded: conflict-free reads
+  constexpr int ROWB = D + 8;             // LDS row stride (2-byte elements), padded: conflict-free reads
   constexpr int CH = D / 8;               // 16-byte chunks per key-mean row
   constexpr int TILE_CH = 32 * CH;        // chunks per plane per 32-key tile
   constexpr int NCH = (TILE_CH + kScoreT - 1) / kScoreT;  // per thread per plane
-  __shared__ __align__(16) uint16_t khi[kScoreStages][32 * ROWB];
-  __shared__ __align__(16) uint16_t klo[kScoreStages][32 * ROWB];
+  __shared__ __align__(16) uint16_t ring[kScoreStages][2][32 * ROWB];
   __shared__ float a_lds[ROWS];
 
   const int gid = xcd_remap(blockIdx.x, n_groups);
@@ -57,9 +60,7 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
   const int cc = crow % C;
   const bool rvalid = qb < n_qb;
   const int64_t prow = (int64_t)bh * n_qb + qb;
-  bf16x8 mh[KS], ml[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
+  auto mu_slice = [&](int s, float (&x)[8]) {
     f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
     if (rvalid) {
       const float* src = mu + (prow * C + cc) * D + 16 * s + 8 * hh;
@@ -67,14 +68,8 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
       v1 = *reinterpret_cast<const f32x4*>(src + 4);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float x = (i < 4 ? v0[i] : v1[i - 4]) * scale_log2;
-      const uint32_t hb = f32_to_bf16_bits(x);
-      const uint32_t lb = f32_to_bf16_bits(x - bf16_bits_to_f32(hb));
-      mh[s][i] = __builtin_bit_cast(__bf16, (uint16_t)hb);
-      ml[s][i] = __builtin_bit_cast(__bf16, (uint16_t)lb);
-    }
-  }
+    for (int i = 0; i < 8; ++i) x[i] = (i < 4 ? v0[i] : v1[i - 4]) * scale_log2;
+  };
   const float wc = rvalid ? w[prow * C + cc] : 0.f;
 
   const uint16_t* hbase = kplanes + (int64_t)bh * n_kbs * D;
@@ -82,101 +77,135 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
   const int n_tiles = (n_kbs + 31) / 32;
   const int tlast = n_tiles - 1;
 
-  // Tile pipeline: tile t is computed from LDS stage t%3.  Two register sets
-  // alternate (the loop is unrolled by two so they stay in registers): at the
-  // top of iteration t the set holding tile t+2 goes to stage (t+2)%3 (last
-  // read in iteration t-1, which ended with a barrier) and the same set is
-  // reloaded with tile t+4, so every load has two iterations to land.
-  struct Regs {
-    u32x4 h[NCH], l[NCH];
+  auto kop = [&](const uint16_t* base, int s) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(base + l32 * ROWB + 16 * s + 8 * hh);
   };
-  Regs ra, rb;
-  auto load_tile = [&](Regs& r, int tile) {
+
+  // One pipelined pass over the planes p0 and p1.  Tile t sits in LDS
+  // stage t%3.  Two register sets alternate (the loop is unrolled by two so
+  // they stay in registers): the set holding tile t+2 goes to stage (t+2)%3
+  // at the top of the half-iteration for tile t and is reloaded with tile
+  // t+4, so every load has two half-iterations to land.  `mma(stage)` forms
+  // a tile's logits from LDS, `fix(x, tile)` masks keys past the end (a
+  // small block of its own), `epi(x, tile)` consumes them; mma of tile t+1
+  // runs in the half-iteration of tile t (stage (t+1)%3 was stored before the
+  // previous barrier, and stage (t+2)%3 was last read one half-iteration
+  // earlier still).
+  auto run_pass = [&](const uint16_t* p0, const uint16_t* p1, auto&& mma, auto&& fix, auto&& epi) {
+    constexpr int NP = 2;
+    struct Regs {
+      u32x4 v[NP][NCH];
+    };
+    Regs ra, rb;
+    auto load_tile = [&](Regs& r, int tile) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int q = i * kScoreT + t;
-      int key = 32 * tile + q / CH;
-      key = key < n_kbs ? key : n_kbs - 1;  // rows past the end are masked later
-      const int64_t off = (int64_t)key * D + 8 * (q % CH);
-      if (q < TILE_CH) {
-        r.h[i] = *reinterpret_cast<const u32x4*>(hbase + off);
-        r.l[i] = *reinterpret_cast<const u32x4*>(lbase + off);
+      for (int i = 0; i < NCH; ++i) {
+        const int q = i * kScoreT + t;
+        int key = 32 * tile + q / CH;
+        key = key < n_kbs ? key : n_kbs - 1;  // rows past the end are masked later
+        const int64_t off = (int64_t)key * D + 8 * (q % CH);
+        if (q < TILE_CH) {
+          r.v[0][i] = *reinterpret_cast<const u32x4*>(p0 + off);
+          r.v[1][i] = *reinterpret_cast<const u32x4*>(p1 + off);
+        }
       }
-    }
-  };
-  auto store_tile = [&](const Regs& r, int stage) {
+    };
+    auto store_tile = [&](const Regs& r, int stage) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int q = i * kScoreT + t;
-      if (q < TILE_CH) {
-        const int o = (q / CH) * ROWB + 8 * (q % CH);
-        *reinterpret_cast<u32x4*>(&khi[stage][o]) = r.h[i];
-        *reinterpret_cast<u32x4*>(&klo[stage][o]) = r.l[i];
+      for (int i = 0; i < NCH; ++i) {
+        const int q = i * kScoreT + t;
+        if (q < TILE_CH) {
+          const int o = (q / CH) * ROWB + 8 * (q % CH);
+#pragma unroll
+          for (int pl = 0; pl < NP; ++pl) *reinterpret_cast<u32x4*>(&ring[stage][pl][o]) = r.v[pl][i];
+        }
       }
-    }
-  };
-  auto kop = [&](const uint16_t* base, int s) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(base + l32 * ROWB + 16 * s + 8 * hh);
-  };
-  auto prologue = [&]() {
+    };
     load_tile(ra, 0);
     store_tile(ra, 0);
     load_tile(rb, min(1, tlast));
-    store_tile(rb, 1 % kScoreStages);
+    store_tile(rb, 1);
     load_tile(ra, min(2, tlast));
     load_tile(rb, min(3, tlast));
     __syncthreads();
-  };
-  // one pipelined pass; `body(tile, stage)` computes a tile
-  auto run_pass = [&](auto&& body) {
-    prologue();
-    int stage = 0;
+    f32x16 xa = mma(0), xb;
+    int st = 0;  // stage of `tile`
+    auto nxt = [](int s) { return s == kScoreStages - 1 ? 0 : s + 1; };
+    // Each half-iteration's MFMAs and exp2 work form one branch-free block;
+    // the MFMAs past the last tile read a stale stage and are discarded.
     for (int tile = 0; tile < n_tiles; tile += 2) {
-      store_tile(ra, (stage + 2) % kScoreStages);
+      const int s1 = nxt(st), s2 = nxt(s1);
+      store_tile(ra, s2);
       load_tile(ra, min(tile + 4, tlast));
-      body(tile, stage);
+      fix(xa, tile);
+      xb = mma(s1);
+      epi(xa, tile);
       __syncthreads();
-      stage = (stage + 1) % kScoreStages;
       if (tile + 1 < n_tiles) {
-        store_tile(rb, (stage + 2) % kScoreStages);
+        store_tile(rb, st);  // stage of tile + 3
         load_tile(rb, min(tile + 5, tlast));
-        body(tile + 1, stage);
+        fix(xb, tile + 1);
+        xa = mma(s2);
+        epi(xb, tile + 1);
         __syncthreads();
-        stage = (stage + 1) % kScoreStages;
       }
+      st = s2;
     }
   };
 
+  bf16x8 mh[KS], ml[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    float x[8];
+    mu_slice(s, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 hb = (__bf16)x[i];
+      mh[s][i] = hb;
+      ml[s][i] = (__bf16)(x[i] - (float)hb);
+    }
+  }
+
   // ---------------- pass 1: softmax normaliser of every centroid ----------------
   float m_run = -INFINITY, s_run = 0.f;
-  run_pass([&](int tile, int stage) {
-    // one accumulation chain: the small cross terms first, then hi*hi
-    f32x16 x = {};
+  {
+    auto mma1 = [&](int stage) {
+      // one accumulation chain: the small cross terms first, then hi*hi
+      f32x16 x = {};
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 kh = kop(khi[stage], s), kl = kop(klo[stage], s);
-      x = mfma_bf16_32x32x16(kl, mh[s], x);
-      x = mfma_bf16_32x32x16(kh, ml[s], x);
-    }
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 kh = __builtin_bit_cast(bf16x8, kop(ring[stage][0], s));
+        const bf16x8 kl = __builtin_bit_cast(bf16x8, kop(ring[stage][1], s));
+        x = mfma_bf16_32x32x16(kl, mh[s], x);
+        x = mfma_bf16_32x32x16(kh, ml[s], x);
+      }
 #pragma unroll
-    for (int s = 0; s < KS; ++s) x = mfma_bf16_32x32x16(kop(khi[stage], s), mh[s], x);
-    // lane: centroid l32, keys 32*tile + 8*(v/4) + 4*hh + v%4
-    if (32 * tile + 32 > n_kbs) {  // only the last tile has keys past the end
+      for (int s = 0; s < KS; ++s)
+        x = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, kop(ring[stage][0], s)), mh[s], x);
+      return x;
+    };
+    auto fix1 = [&](f32x16& x, int tile) {
+      // lane: centroid l32, keys 32*tile + 8*(v/4) + 4*hh + v%4; only the last
+      // tile has keys past the end (clamped copies of the last block)
+      if (32 * tile + 32 > n_kbs) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (32 * tile + 8 * (v >> 2) + 4 * hh + (v & 3) >= n_kbs) x[v] = -INFINITY;
-    }
-    float tmax = -INFINITY;
+        for (int v = 0; v < 16; ++v)
+          if (32 * tile + 8 * (v >> 2) + 4 * hh + (v & 3) >= n_kbs) x[v] = -INFINITY;
+      }
+    };
+    auto epi1 = [&](const f32x16& x, int tile) {
+      float tmax = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, x[v]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (tmax > m_run) {
-      s_run *= __builtin_amdgcn_exp2f(m_run - tmax);
-      m_run = tmax;
-    }
+      for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, x[v]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // finite: every tile has a valid key
+      const float m_new = fmaxf(m_run, tmax);
+      s_run *= __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s_run += __builtin_amdgcn_exp2f(x[v] - m_run);
-  });
+      for (int v = 0; v < 16; ++v) s_run += __builtin_amdgcn_exp2f(x[v] - m_run);
+    };
+    run_pass(hbase, lbase, mma1, fix1, epi1);
+  }
   s_run += __shfl_xor(s_run, 32);
   // log2 of (w_c / normaliser); -inf for an empty cluster
   const float a_c = log2f(wc) - (m_run + log2f(s_run));
@@ -187,17 +216,33 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
   float a_v[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) a_v[v] = a_lds[32 * wv + 8 * (v >> 2) + 4 * hh + (v & 3)];
-  float* srow_base = S + ((int64_t)bh * n_qb) * n_kbs;
-  run_pass([&](int tile, int stage) {
+  // S rows of this work-group's query blocks through a bounds-checked buffer:
+  // stores past the last row are dropped, keys past the end get an offset
+  // beyond the range
+  const int rows_here = min(G, n_qb - qb0);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      S + ((int64_t)bh * n_qb + qb0) * n_kbs, (short)0, rows_here * n_kbs * 4, 0x00020000);
+  auto put = [&](int qrel, int key, float v) {
+    const uint32_t off = key < n_kbs ? (uint32_t)(qrel * n_kbs + key) * 4u : 0x80000000u;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), srs, off, 0, 0);
+  };
+  auto mma2 = [&](int stage) {
+    // one accumulation chain: the small cross terms first, then hi*hi
     f32x16 x = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const bf16x8 kh = kop(khi[stage], s), kl = kop(klo[stage], s);
+      const bf16x8 kh = __builtin_bit_cast(bf16x8, kop(ring[stage][0], s));
+      const bf16x8 kl = __builtin_bit_cast(bf16x8, kop(ring[stage][1], s));
       x = mfma_bf16_32x32x16(mh[s], kl, x);
       x = mfma_bf16_32x32x16(ml[s], kh, x);
     }
 #pragma unroll
-    for (int s = 0; s < KS; ++s) x = mfma_bf16_32x32x16(mh[s], kop(khi[stage], s), x);
+    for (int s = 0; s < KS; ++s)
+      x = mfma_bf16_32x32x16(mh[s], __builtin_bit_cast(bf16x8, kop(ring[stage][0], s)), x);
+    return x;
+  };
+  auto fix2 = [](f32x16&, int) {};
+  auto epi2 = [&](const f32x16& x, int tile) {
     // lane: key 32*tile + l32, centroid rows 32*wv + 8*(v/4) + 4*hh + v%4
     float p[16];
 #pragma unroll
@@ -214,8 +259,7 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
         const int g = 2 * hh + gg;
-        const int q = qb0 + 4 * wv + g;
-        if (q < n_qb && key < n_kbs) srow_base[(int64_t)q * n_kbs + key] = tot[g];
+        put(4 * wv + g, key, tot[g]);
       }
     } else {
       // C == 16: rows 16gp..16gp+15 = one query block
@@ -227,10 +271,10 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
         for (int v = 8 * gp; v < 8 * gp + 8; ++v) part += p[v];
         tot[gp] = part + __shfl_xor(part, 32);
       }
-      const int q = qb0 + 2 * wv + hh;
-      if (q < n_qb && key < n_kbs) srow_base[(int64_t)q * n_kbs + key] = tot[hh];
+      put(2 * wv + hh, key, tot[hh]);
     }
-  });
+  };
+  run_pass(hbase, lbase, mma2, fix2, epi2);
 }
 
 template <int D, int C>
