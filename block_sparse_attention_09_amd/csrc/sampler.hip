@@ -10,7 +10,8 @@
 // Per plan row (one work-group, the score row staged in LDS):
 //   * pi: m = budget * n expected blocks; repeat c = (m - #certain) /
 //     sum(uncertain positive scores) and make every uncertain block with
-//     c*s >= 1 certain, until none is added.  The certain set is always a top
+//     c*s >= 1 certain, until none is added (the first round reads the row
+//     once: count, sum and maximum together).  The certain set is always a top
 //     set of the scores, so it is held as a threshold theta (certain iff
 //     s >= theta).  float64 throughout; sums are fixed-order tree reductions,
 //     so every run gives the same bits.
@@ -118,26 +119,46 @@ __device__ PiSolve solve_pi(const float* s, int n, double budget, Red& red) {
     ps.mode = 0;
     return ps;
   }
+  // one pass: positive count, fp64 sum of the positive scores (the first
+  // iteration's sum, same accumulation order as the loop below) and the
+  // largest score
   int npos = 0;
-  for (int j = threadIdx.x; j < n; j += kSampT) npos += s[j] > 0.f;
+  double part = 0.0;
+  float smax = 0.f;
+  for (int j = threadIdx.x; j < n; j += kSampT) {
+    const float v = s[j];
+    if (v > 0.f) {
+      ++npos;
+      part += (double)v;
+      smax = fmaxf(smax, v);
+    }
+  }
   npos = block_sum_i32(npos, red);
   if (m >= (double)npos) {
     ps.mode = 1;
     return ps;
   }
   ps.mode = 2;
+  double sum = block_sum_f64(part, red);
+  smax = -block_min_f32(-smax, red);
   int ncert = 0;
   float theta = INFINITY;
-  for (;;) {
-    double part = 0.0;
-    for (int j = threadIdx.x; j < n; j += kSampT) {
-      const float v = s[j];
-      if (v > 0.f && v < theta) part += (double)v;
+  for (bool first = true;; first = false) {
+    if (!first) {
+      part = 0.0;
+      for (int j = threadIdx.x; j < n; j += kSampT) {
+        const float v = s[j];
+        if (v > 0.f && v < theta) part += (double)v;
+      }
+      sum = block_sum_f64(part, red);
     }
-    const double sum = block_sum_f64(part, red);
     if (!(sum > 0.0)) break;
     const double c = (m - (double)ncert) / sum;
     ps.c = c;
+    // no uncertain score reaches 1/c: nothing more becomes certain (c*s is
+    // monotonic in s, so the largest score decides; first iteration only,
+    // where every positive score is uncertain)
+    if (first && c * (double)smax < 1.0) break;
     float cand = INFINITY;
     for (int j = threadIdx.x; j < n; j += kSampT) {
       const float v = s[j];
