@@ -15,8 +15,10 @@
 //     set of the scores, so it is held as a threshold theta (certain iff
 //     s >= theta).  float64 throughout; sums are fixed-order tree reductions,
 //     so every run gives the same bits.
-//   * draws: block j uses word j%4 of Philox4x64-10(counter (j/4, qb, h, b),
-//     key (seed, 0)); kept iff its top 53 bits < pi_j * 2^53 (exact compare).
+//   * draws: block j uses words 2(j%2), 2(j%2)+1 of Philox4x32-10 with
+//     counter (j/2, qb, h, b) and key (seed low, seed high) as one 53-bit
+//     uniform (32 bits from the first word, the top 21 of the second); kept
+//     iff it is < pi_j * 2^53 (exact compare).
 // k_sip_count solves pi, draws, and records the row's kept-block bitmask, its
 // count and its solve (mode, c, theta); k_scan turns counts into row_ptr (and
 // flags a plan that exceeds its capacity); k_sip_fill walks the bitmask and
@@ -29,24 +31,25 @@
 
 namespace abatt {
 
-// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): 10 rounds of two
-// 64x64->128-bit multiplies with a Weyl-sequence key schedule.
-__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
-  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): per round two 32x32->64
+// multiplies (one v_mad_u64_u32 each), the high halves XORed into the other
+// words with the key, a Weyl key schedule, ten rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) {
       k0 += W0;
       k1 += W1;
     }
-    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
-    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
-    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    const uint64_t p0 = (uint64_t)M0 * c[0], p1 = (uint64_t)M1 * c[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
     c[0] = n0;
-    c[1] = lo1;
+    c[1] = (uint32_t)p1;
     c[2] = n2;
-    c[3] = lo0;
+    c[3] = (uint32_t)p0;
   }
 }
 
@@ -187,19 +190,23 @@ __device__ __forceinline__ const float* stage_row(const float* g, int n, float* 
   }
 }
 
-// Kept-bit mask (4 bits) of the four blocks of Philox group g.
+// Kept-bit mask (4 bits) of blocks 4g..4g+3: two Philox calls (counters 2g
+// and 2g+1), each giving two 53-bit uniforms (words 0,1 and 2,3).
 __device__ __forceinline__ uint32_t draw_group(const float* s, int n, int g, int qb, int h, int b,
                                                uint64_t seed, const PiSolve& ps) {
-  uint64_t c[4] = {(uint64_t)g, (uint64_t)qb, (uint64_t)h, (uint64_t)b};
-  philox4x64_10(c, seed, 0ull);
   uint32_t mask = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = 4 * g + i;
-    if (j < n) {
-      const double pi = pi_of(s[j], ps);
-      const double u = (double)(c[i] >> 11);
-      if (u < pi * kTwo53) mask |= 1u << i;
+  for (int i = 0; i < 2; ++i) {
+    uint32_t c[4] = {(uint32_t)(2 * g + i), (uint32_t)qb, (uint32_t)h, (uint32_t)b};
+    philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int j = 4 * g + 2 * i + k;
+      if (j < n) {
+        const double pi = pi_of(s[j], ps);
+        const double u = (double)(((uint64_t)c[2 * k] << 21) | (c[2 * k + 1] >> 11));
+        if (u < pi * kTwo53) mask |= 1u << (2 * i + k);
+      }
     }
   }
   return mask;

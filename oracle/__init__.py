@@ -6,6 +6,6 @@ this package.  It shares no code with the GPU library.
 from .abatt_oracle import *  # noqa: F401,F403
 from .abatt_oracle import (Problem, Plan, attend, attend_row, dense, dense_rows,  # noqa: F401
                            ht_estimates, ibcs_scores, inclusion_probabilities,
-                           key_block_means, kmeans, philox4x64_10, plan,
+                           key_block_means, kmeans, philox4x32_10, plan,
                            plan_from_scores, query_clusters, sample_row,
                            block_scores, block_uniforms, unflatten_row)

@@ -28,8 +28,9 @@ the design notes):
     normalised per centroid over the sparse key blocks, then rounded to fp32;
   * budget b means m = b * n_sparse_blocks expected blocks per row; b = 1
     takes every block; independent (Poisson) draws, so the row count varies;
-  * randomness: Philox4x64-10, counter (j//4, qb, h, b), key (seed, 0), word
-    j%4, 53-bit uniform compared exactly against pi * 2^53;
+  * randomness: Philox4x32-10, counter (j//2, qb, h, b), key (seed low,
+    seed high), words 2(j%2) and 2(j%2)+1 as one 53-bit uniform compared
+    exactly against pi * 2^53;
   * trailing text tokens (if any) form forced key blocks with pi = 1 that are
     not scored and not counted in the budget.
 
@@ -44,9 +45,6 @@ import math
 from typing import List, Optional, Tuple
 
 import numpy as np
-
-M64 = (1 << 64) - 1
-
 
 @dataclasses.dataclass(frozen=True)
 class Problem:
@@ -244,62 +242,50 @@ def inclusion_probabilities(s32: np.ndarray, budget: float) -> np.ndarray:
     return np.where(certain, 1.0, np.where(pos & ~certain, c * s, 0.0))
 
 
-# Philox4x64-10 (Salmon, Moraes, Dror, Shaw: "Parallel random numbers: as easy
-# as 1, 2, 3", SC'11): two 64x64->128 multiplies per round, a Weyl key
-# schedule, ten rounds.
-PHILOX_M0 = 0xD2E7470EE14C6C93
-PHILOX_M1 = 0xCA5A826395121157
-PHILOX_W0 = 0x9E3779B97F4A7C15
-PHILOX_W1 = 0xBB67AE8584CAA73B
+# Philox4x32-10 (Salmon, Moraes, Dror, Shaw: "Parallel random numbers: as easy
+# as 1, 2, 3", SC'11): per round two 32x32->64 multiplies of counter words 0
+# and 2 by fixed multipliers, the high halves XORed into the other words with
+# the key, a Weyl key schedule between rounds, ten rounds.
+PHILOX_M0 = 0xD2511F53
+PHILOX_M1 = 0xCD9E8D57
+PHILOX_W0 = 0x9E3779B9
+PHILOX_W1 = 0xBB67AE85
+M32 = 0xFFFFFFFF
 
 
-def _mulhilo64(a: np.ndarray, b: int) -> Tuple[np.ndarray, np.ndarray]:
-    """(high, low) 64-bit halves of the 128-bit product, uint64 arrays."""
-    m32 = np.uint64(0xFFFFFFFF)
+def philox4x32_10(ctr: Tuple[np.ndarray, ...], key: Tuple[int, int]) -> Tuple[np.ndarray, ...]:
+    """Philox4x32 with 10 rounds on arrays of counters (32-bit words held in
+    uint64); returns the 4 output words (uint64 arrays, values < 2^32)."""
+    m32 = np.uint64(M32)
     s32 = np.uint64(32)
-    a = a.astype(np.uint64)
-    b_lo, b_hi = np.uint64(b & 0xFFFFFFFF), np.uint64(b >> 32)
-    a_lo, a_hi = a & m32, a >> s32
-    ll = a_lo * b_lo
-    hl = a_hi * b_lo
-    lh = a_lo * b_hi
-    hh = a_hi * b_hi
-    t = hl + (ll >> s32)
-    u = lh + (t & m32)
-    hi = hh + (t >> s32) + (u >> s32)
-    lo = (u << s32) | (ll & m32)
-    return hi, lo
-
-
-def philox4x64_10(ctr: Tuple[np.ndarray, ...], key: Tuple[int, int]) -> Tuple[np.ndarray, ...]:
-    """Philox4x64 with 10 rounds on arrays of counters; returns 4 uint64 words."""
-    with np.errstate(over="ignore"):
-        c0, c1, c2, c3 = (np.asarray(x, dtype=np.uint64) for x in ctr)
-        k0, k1 = key[0] & M64, key[1] & M64
-        for rnd in range(10):
-            if rnd > 0:
-                k0 = (k0 + PHILOX_W0) & M64
-                k1 = (k1 + PHILOX_W1) & M64
-            hi0, lo0 = _mulhilo64(c0, PHILOX_M0)
-            hi1, lo1 = _mulhilo64(c2, PHILOX_M1)
-            c0, c1, c2, c3 = (hi1 ^ c1 ^ np.uint64(k0), lo1,
-                              hi0 ^ c3 ^ np.uint64(k1), lo0)
+    c0, c1, c2, c3 = (np.asarray(x, dtype=np.uint64) & m32 for x in ctr)
+    k0, k1 = key[0] & M32, key[1] & M32
+    for rnd in range(10):
+        if rnd > 0:
+            k0 = (k0 + PHILOX_W0) & M32
+            k1 = (k1 + PHILOX_W1) & M32
+        p0 = c0 * np.uint64(PHILOX_M0)      # < 2^64: exact in uint64
+        p1 = c2 * np.uint64(PHILOX_M1)
+        c0, c1, c2, c3 = ((p1 >> s32) ^ c1 ^ np.uint64(k0), p1 & m32,
+                          (p0 >> s32) ^ c3 ^ np.uint64(k1), p0 & m32)
     return c0, c1, c2, c3
 
 
 def block_uniforms(b: int, h: int, qb: int, n: int, seed: int) -> np.ndarray:
     """53-bit uniform integers (uint64) for sparse key blocks 0..n-1 of a row.
 
-    Block j uses word j%4 of Philox4x64-10(counter=(j//4, qb, h, b),
-    key=(seed, 0)) and keeps its top 53 bits.
+    Block j uses words 2(j%2) and 2(j%2)+1 of Philox4x32-10 with counter
+    (j//2, qb, h, b) and key (low, high 32 bits of the seed): the first word
+    gives the top 32 bits, the top 21 bits of the second the rest.
     """
-    groups = -(-n // 4)
-    g = np.arange(groups, dtype=np.uint64)
-    z = np.zeros(groups, dtype=np.uint64)
-    words = philox4x64_10((g, z + np.uint64(qb), z + np.uint64(h), z + np.uint64(b)),
-                          (seed & M64, 0))
-    x = np.stack(words, axis=1).reshape(-1)[:n]
-    return x >> np.uint64(11)
+    pairs = -(-n // 2)
+    g = np.arange(pairs, dtype=np.uint64)
+    z = np.zeros(pairs, dtype=np.uint64)
+    w0, w1, w2, w3 = philox4x32_10((g, z + np.uint64(qb), z + np.uint64(h), z + np.uint64(b)),
+                                   (seed & M32, (seed >> 32) & M32))
+    hi = np.stack([w0, w2], axis=1).reshape(-1)[:n]
+    lo = np.stack([w1, w3], axis=1).reshape(-1)[:n]
+    return (hi << np.uint64(21)) | (lo >> np.uint64(11))
 
 
 def sample_row(s32: np.ndarray, budget: float, b: int, h: int, qb: int, seed: int,

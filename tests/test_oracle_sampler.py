@@ -1,13 +1,16 @@
 """Pins of the oracle's SIP sampler: inclusion probabilities, Philox, draws, plan.
 
 Pins: the pages' 25%-counts-as-four example, brute force over cut-offs,
-numpy's Philox and the Random123 known answer, the sampling law over many
-seeds, and the Horvitz-Thompson expectation by exact enumeration.
+the Random123 known answers for Philox4x32-10 and rocRAND's independent
+implementation of it, the sampling law over many seeds, and the
+Horvitz-Thompson expectation by exact enumeration.
 """
 import itertools
 import json
 import math
 import os
+import shutil
+import subprocess
 
 import numpy as np
 import pytest
@@ -108,39 +111,69 @@ def test_inclusion_probabilities_special_cases():
     np.testing.assert_allclose(np.delete(pi, 7), 3.0 / 39, rtol=1e-6)
 
 
-# Philox4x64-10 known answer from the Random123 distribution (counter 0, key 0)
-R123_KAT_ZERO = (0x16554D9ECA36314C, 0xDB20FE9D672D0FDC, 0xD7E772CEE186176B, 0x7E68B68AEC7BA23B)
+# Philox4x32-10 known answers from the Random123 distribution (the
+# generator's authors): counter, key -> the four output words
+R123_KAT = [
+    ((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+    ((0xFFFFFFFF,) * 4, (0xFFFFFFFF, 0xFFFFFFFF), (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+    ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+     (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1)),
+]
 
 
-def test_philox_known_answer():
-    z = np.zeros(1, np.uint64)
-    out = oracle.philox4x64_10((z, z, z, z), (0, 0))
-    assert tuple(int(w[0]) for w in out) == R123_KAT_ZERO
+def test_philox_known_answers():
+    for ctr, key, want in R123_KAT:
+        out = oracle.philox4x32_10(tuple(np.array([c], np.uint64) for c in ctr), key)
+        assert tuple(int(w[0]) for w in out) == want
 
 
-def test_philox_matches_numpy():
+@pytest.fixture(scope="module")
+def rocrand_philox(tmp_path_factory):
+    """Runs rocRAND's header-only Philox4x32-10 engine on the host."""
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    header = "/opt/rocm/include/rocrand/rocrand_philox4x32_10.h"
+    if not (os.path.exists(hipcc) and os.path.exists(header)):
+        pytest.skip("hipcc or the rocRAND headers are not available")
+    exe = str(tmp_path_factory.mktemp("philox") / "philox_ref")
+    src = os.path.join(os.path.dirname(__file__), "philox_ref.cpp")
+    r = subprocess.run([hipcc, "-O1", src, "-o", exe], capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("could not build the rocRAND reference: " + r.stderr[-500:])
+
+    def run(queries):
+        text = "".join(f"{s} {u} {o}\n" for s, u, o in queries)
+        out = subprocess.run([exe], input=text, capture_output=True, text=True, check=True)
+        return [tuple(int(x, 16) for x in line.split()) for line in out.stdout.splitlines()]
+    return run
+
+
+def test_philox_matches_rocrand(rocrand_philox):
+    # the engine at (seed, subsequence, offset) = Philox4x32-10 with counter
+    # (offset/4 low, offset/4 high, subsequence low, subsequence high) and key
+    # (seed low, seed high)
     rng = np.random.default_rng(1)
-    M = (1 << 64) - 1
-    for _ in range(100):
-        c = [int(x) for x in rng.integers(0, 2 ** 63, 4, dtype=np.uint64)]
-        k = [int(x) for x in rng.integers(0, 2 ** 63, 2, dtype=np.uint64)]
-        ctr = c[0] + (c[1] << 64) + (c[2] << 128) + (c[3] << 192)
-        # numpy advances its counter once before producing the first block
-        ref = np.random.Philox(counter=ctr, key=k[0] + (k[1] << 64)).random_raw(4)
-        nxt = ctr + 1
-        words = tuple(np.array([(nxt >> (64 * i)) & M], np.uint64) for i in range(4))
-        out = oracle.philox4x64_10(words, (k[0], k[1]))
-        assert [int(w[0]) for w in out] == [int(x) for x in ref]
+    cases = [[int(x) for x in rng.integers(0, 2 ** 32, 6, dtype=np.uint64)] for _ in range(64)]
+    for cs in cases:
+        cs[1] >>= 2  # the engine's offset is 64-bit: 4 * counter must fit
+    queries = [(k0 | (k1 << 32), c2 | (c3 << 32), 4 * (c0 | (c1 << 32)))
+               for c0, c1, c2, c3, k0, k1 in cases]
+    ref = rocrand_philox(queries)
+    for (c0, c1, c2, c3, k0, k1), want in zip(cases, ref):
+        out = oracle.philox4x32_10(tuple(np.array([c], np.uint64) for c in (c0, c1, c2, c3)),
+                                   (k0, k1))
+        assert tuple(int(w[0]) for w in out) == want
 
 
-def test_block_uniforms_layout():
-    # block j of row (b,h,qb) = word j%4 of the block at counter (j//4, qb, h, b)
-    b, h, qb, seed = 1, 3, 17, 12345
-    u = oracle.block_uniforms(b, h, qb, 10, seed)
-    for j in range(10):
-        ctr = (j // 4) + (qb << 64) + (h << 128) + (b << 192)
-        ref = np.random.Philox(counter=ctr - 1, key=seed).random_raw(4)
-        assert int(u[j]) == int(ref[j % 4]) >> 11
+def test_block_uniforms_layout(rocrand_philox):
+    # block j of row (b,h,qb): words 2(j%2), 2(j%2)+1 at counter (j//2, qb, h, b)
+    for b, h, qb, seed in [(1, 3, 17, 12345), (0, 39, 590, (1 << 63) + 977)]:
+        u = oracle.block_uniforms(b, h, qb, 11, seed)
+        words = rocrand_philox([(seed, h | (b << 32), 4 * (j // 2 + (qb << 32))) for j in range(11)])
+        for j in range(11):
+            w = words[j]
+            hi, lo = w[2 * (j % 2)], w[2 * (j % 2) + 1]
+            assert int(u[j]) == (hi << 21) | (lo >> 11)
+            assert int(u[j]) < 2 ** 53
 
 
 def test_sampling_law():
