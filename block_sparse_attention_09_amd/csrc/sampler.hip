@@ -293,6 +293,9 @@ __global__ __launch_bounds__(kSampT) void k_sip_fill(const float* __restrict__ S
                                                     int32_t* __restrict__ col_idx,
                                                     float* __restrict__ logw) {
   __shared__ int wtot[kSampWaves];
+  // kept blocks of one pass over kSampT mask words, as offsets from the
+  // pass's first block (< 32 * kSampT = 16384, so 16 bits suffice)
+  __shared__ uint16_t list[32 * kSampT];
   if (*status != 0) return;  // plan exceeded its capacity: nothing is written
   const int r = blockIdx.x;
   const int words = (n + 31) / 32;
@@ -320,16 +323,22 @@ __global__ __launch_bounds__(kSampT) void k_sip_fill(const float* __restrict__ S
       if (q < w) before += wtot[q];
       tot += wtot[q];
     }
-    int64_t pos = start + run + before + incl - k;
+    // compact this word's kept blocks (ascending) into the list
+    int pos = before + incl - k;
     uint32_t mm = m;
     while (mm) {
       const int bit = __ffs(mm) - 1;
       mm &= mm - 1;
-      const int j = 32 * wi + bit;
+      list[pos++] = (uint16_t)(32 * t + bit);
+    }
+    __syncthreads();
+    // every thread takes kept blocks i, i + kSampT, ...: coalesced writes
+    const int64_t out = start + run;
+    for (int i = t; i < tot; i += kSampT) {
+      const int j = 32 * base + list[i];
       const double pi = pi_of(srow[j], ps);
-      col_idx[pos] = j;
-      logw[pos] = pi == 1.0 ? 0.0f : (float)(-log(pi));
-      ++pos;
+      col_idx[out + i] = j;
+      logw[out + i] = pi == 1.0 ? 0.0f : (float)(-log(pi));
     }
     run += tot;
     __syncthreads();
