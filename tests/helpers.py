@@ -54,13 +54,29 @@ TOL = {"bf16": (1e-2, 1e-3), "f32": (1e-4, 1e-4)}
 LSE_TOL = {"bf16": 2e-3, "f32": 1e-4}
 
 
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 values at |x| (normal range)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
 def check_output(o_gpu: torch.Tensor, o_ref: np.ndarray, dtype: str, what: str):
+    """Output bar: max-abs and mean-rel against the oracle rounded like the
+    output.  Two values rounded to bf16 can sit one bf16 step apart when the
+    exact result lies near a rounding boundary, and above |x| = 2 that step
+    (2^-6) exceeds the 1e-2 absolute bar, so for bf16 each element may also
+    differ by one step of its reference."""
     got = o_gpu.float().cpu().numpy().astype(np.float64)
     ref = round_ref(o_ref, dtype)
     mx, mr = errors(got, ref)
     say(f"{what}: max-abs {mx:.3e} mean-rel {mr:.3e}")
     tol = TOL[dtype]
-    assert mx <= tol[0] and mr <= tol[1], (what, mx, mr)
+    assert mr <= tol[1], (what, mx, mr)
+    if mx > tol[0]:
+        fin = np.isfinite(ref)
+        allowed = np.maximum(tol[0], bf16_ulp(ref[fin])) if dtype == "bf16" else tol[0]
+        over = np.abs(got[fin] - ref[fin]) > allowed
+        assert not over.any(), (what, mx, mr, int(over.sum()))
     return mx, mr
 
 
