@@ -65,7 +65,10 @@ def test_key_means_invariants():
     np.testing.assert_array_equal(oracle.key_block_means(K, probf), kbar[:, :, :14])
 
 
-@pytest.mark.parametrize("seed", range(6))
+# seeds whose clustering never empties a cluster (scikit-learn relocates an
+# empty cluster; the method keeps its centroid, which the fixed-point and
+# edge-case tests below cover)
+@pytest.mark.parametrize("seed", range(1, 7))
 def test_kmeans_matches_sklearn(seed):
     rng = np.random.default_rng(seed)
     n, d, C, it = 128, 16, 8, 10
@@ -74,8 +77,7 @@ def test_kmeans_matches_sklearn(seed):
     init = X[[(c * n) // C for c in range(C)]]
     km = KMeans(n_clusters=C, init=init, n_init=1, max_iter=it, tol=0.0,
                 algorithm="lloyd").fit(X)
-    if np.any(np.bincount(km.labels_, minlength=C) == 0) or np.any(counts == 0):
-        pytest.skip("a cluster emptied; the two handle that differently")
+    assert np.all(np.bincount(km.labels_, minlength=C) > 0) and np.all(counts > 0)
     np.testing.assert_allclose(mu, km.cluster_centers_, rtol=1e-10, atol=1e-12)
     assert counts.sum() == n
 
