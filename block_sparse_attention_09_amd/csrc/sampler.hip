@@ -10,8 +10,8 @@
 // Per plan row (one work-group, the score row staged in LDS):
 //   * pi: m = budget * n expected blocks; repeat c = (m - #certain) /
 //     sum(uncertain positive scores) and make every uncertain block with
-//     c*s >= 1 certain, until none is added (the first round reads the row
-//     once: count, sum and maximum together).  The certain set is always a top
+//     c*s >= 1 certain, until none is added (the first round's count, sum
+//     and maximum are gathered while the row is staged).  The certain set is always a top
 //     set of the scores, so it is held as a threshold theta (certain iff
 //     s >= theta).  float64 throughout; sums are fixed-order tree reductions,
 //     so every run gives the same bits.
@@ -113,7 +113,22 @@ __device__ __forceinline__ double pi_of(float s, const PiSolve& ps) {
   return ps.c * (double)s;
 }
 
-__device__ PiSolve solve_pi(const float* s, int n, double budget, Red& red) {
+// First-round statistics of a row (this thread's share): positive count,
+// fp64 sum of the positive scores, largest score.
+struct RowStats {
+  int npos = 0;
+  double sum = 0.0;
+  float smax = 0.f;
+  __device__ __forceinline__ void add(float v) {
+    if (v > 0.f) {
+      ++npos;
+      sum += (double)v;
+      smax = fmaxf(smax, v);
+    }
+  }
+};
+
+__device__ PiSolve solve_pi(const float* s, int n, double budget, RowStats st, Red& red) {
   PiSolve ps;
   ps.c = 0.0;
   ps.theta = INFINITY;
@@ -122,21 +137,9 @@ __device__ PiSolve solve_pi(const float* s, int n, double budget, Red& red) {
     ps.mode = 0;
     return ps;
   }
-  // one pass: positive count, fp64 sum of the positive scores (the first
-  // iteration's sum, same accumulation order as the loop below) and the
-  // largest score
-  int npos = 0;
-  double part = 0.0;
-  float smax = 0.f;
-  for (int j = threadIdx.x; j < n; j += kSampT) {
-    const float v = s[j];
-    if (v > 0.f) {
-      ++npos;
-      part += (double)v;
-      smax = fmaxf(smax, v);
-    }
-  }
-  npos = block_sum_i32(npos, red);
+  int npos = block_sum_i32(st.npos, red);
+  double part = st.sum;
+  float smax = st.smax;
   if (m >= (double)npos) {
     ps.mode = 1;
     return ps;
@@ -178,11 +181,32 @@ __device__ PiSolve solve_pi(const float* s, int n, double budget, Red& red) {
   return ps;
 }
 
-// Stage the row in LDS (or read it from global memory when it does not fit).
+// Stage the row in LDS (or read it in place when it does not fit) and gather
+// the first-round statistics on the way: 16-byte loads when the row starts
+// 16-byte aligned, 4-byte loads otherwise.
 template <bool kLds>
-__device__ __forceinline__ const float* stage_row(const float* g, int n, float* lds) {
+__device__ __forceinline__ const float* stage_row(const float* g, int n, float* lds,
+                                                  RowStats& st) {
+  int head = 0;
+  if ((reinterpret_cast<uintptr_t>(g) & 15) == 0) {
+    const int n4 = n >> 2;
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(g);
+    for (int q = threadIdx.x; q < n4; q += kSampT) {
+      const f32x4 v = g4[q];
+      if constexpr (kLds) reinterpret_cast<f32x4*>(lds)[q] = v;
+      st.add(v[0]);
+      st.add(v[1]);
+      st.add(v[2]);
+      st.add(v[3]);
+    }
+    head = 4 * n4;
+  }
+  for (int j = head + threadIdx.x; j < n; j += kSampT) {
+    const float v = g[j];
+    if constexpr (kLds) lds[j] = v;
+    st.add(v);
+  }
   if constexpr (kLds) {
-    for (int j = threadIdx.x; j < n; j += kSampT) lds[j] = g[j];
     __syncthreads();
     return lds;
   } else {
@@ -223,8 +247,9 @@ __global__ __launch_bounds__(kSampT) void k_sip_count(const float* __restrict__ 
   __shared__ Red red;
   const int r = blockIdx.x;
   const int qb = r % n_qb, bh = r / n_qb, h = bh % H, b = bh / H;
-  const float* s = stage_row<kLds>(S + (int64_t)r * n, n, srow);
-  const PiSolve ps = solve_pi(s, n, budget, red);
+  RowStats st;
+  const float* s = stage_row<kLds>(S + (int64_t)r * n, n, srow, st);
+  const PiSolve ps = solve_pi(s, n, budget, st, red);
   const int groups = (n + 3) / 4;
   const int words = (n + 31) / 32;
   uint32_t* mrow = masks + (int64_t)r * words;
