@@ -120,6 +120,9 @@ def main():
     ap.add_argument("--workload", default="wan14b_720p", choices=sorted(CONFIGS))
     ap.add_argument("--budget", type=float, default=None)
     ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="attend reps, each after a 512 MB overwrite that evicts K/V from the "
+                         "Infinity Cache; reported as a median (0 skips)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--probe", choices=["copy"], default=None)
@@ -194,6 +197,33 @@ def main():
     torch.cuda.synchronize()
     plan_ms = s2.elapsed_time(e2) / args.steps
 
+    # attend from a cold Infinity Cache: a 512 MB overwrite before each rep,
+    # outside the event pair; median over the reps
+    attend_cold_ms = None
+    if args.cold_reps > 0:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=q.device)
+        cold = []
+        for i in range(args.cold_reps):
+            scratch.fill_(i & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            ab.attend(q, k, v, pl, problem=prob, out=o)
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b))
+        attend_cold_ms = float(np.median(cold))
+        del scratch
+        log(f"attend from a cold cache: median {attend_cold_ms:.3f} ms over {args.cold_reps} reps")
+
+    # per-row counts of the timed plan: computed tiles include the padding of
+    # each row's last 16-block chunk; useful work excludes the padded query rows
+    # of a head's last query block
+    rp = pl.row_ptr.cpu().numpy().astype(np.int64)
+    row_nnz = np.diff(rp)
+    valid_q = np.minimum(128, wl.N - 128 * (np.arange(prob.R) % prob.n_qb))
+    executed_pairs = int((np.ceil(row_nnz / 16.0) * 16).sum())
+    useful_flop = float((row_nnz * valid_q).sum()) * 4 * 4 * wl.D
+
     dense_ms = None
     if not args.no_dense:
         od = torch.empty_like(q)
@@ -263,6 +293,14 @@ def main():
             "speedup_amortized_vs_dense": (dense_ms / (attend_ms + plan_ms / 4)) if dense_ms else None,
             "dense_mfma_frac": (dense_flop / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if dense_ms else None,
             "attend_flop_per_launch": attend_flop,
+            "attend_ms_cold_median": attend_cold_ms,
+            "attend_mfma_frac_executed_tiles": PAIR_FLOP(D) * executed_pairs / (attend_ms * 1e-3) / 1e12
+                                              / PEAK_BF16_TFLOPS,
+            "attend_mfma_frac_useful": useful_flop / (attend_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            # algorithmic selector traffic: Q and K read, S written once and read
+            # twice (4 + 8 bytes per pair), the plan written
+            "plan_hbm_gbps": (2 * B * H * N * D * 2 + 12 * prob.R * prob.n_kbs + 8 * nnz
+                              + 4 * (prob.R + 1)) / (plan_ms * 1e-3) / 1e9,
         },
         "cpu_baseline": None,
     }
