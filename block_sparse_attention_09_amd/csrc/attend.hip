@@ -58,6 +58,35 @@ __device__ __forceinline__ int vswz(int row) {
   return (4 * (row & 3)) & (D / 8 - 1);
 }
 
+// s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (no wait),
+// lgkmcnt 11:8.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+// Work-group barrier for stages filled by direct-to-LDS loads, which the
+// compiler does not track: wait for all of this wave's vector memory
+// operations and LDS accesses, then s_barrier; the empty asm statements keep
+// the compiler from moving memory operations across it.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 16 bytes per lane from a buffer straight into LDS, lane l's bytes at
+// lds_addr + 16 l.  Written as inline asm so that the compiler does not track
+// it: its own wait insertion would otherwise make every later LDS read wait
+// for it.  The caller waits (dma_barrier) before the stage is read.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, int voff,
+                                                  uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rs), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // Buffer resource for a head's K or V (bounds-checked: loads past the end
 // return zero, which the dense path relies on for its last partial block).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int bytes) {
@@ -74,12 +103,17 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     int n_qb, int n_kb, int R, float scale_log2) {
   constexpr int KS = D / 16;          // QK^T k-steps
   constexpr int DT = D / 32;          // PV output tiles
-  constexpr int KROW = D + 8;         // K tile row stride (bf16), padded
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int SLOTS = 2 * D / 64;   // 16-byte loads per lane per chunk, for K and for V
   constexpr int BPS = 64 / (4 * CPR); // blocks covered by one slot of a wave (1 or 2)
   constexpr int BLOCK_BYTES = 4 * D * 2;
-  __shared__ __align__(16) uint16_t Ks[2][64 * KROW];
+  constexpr int LPB = BLOCK_BYTES / 16;  // lanes of one direct K load per block (64 or 32)
+  constexpr int BPI = 64 / LPB;          // blocks per direct K load (1 or 2)
+  // K tile: row-major, 16-byte slot s of row r stored at s ^ (r % CPR)
+  // (conflict-free operand reads without padding; the direct loads place each
+  // lane's 16 bytes at a fixed LDS position, so the swizzle is chosen through
+  // the source address)
+  __shared__ __align__(16) uint16_t Ks[2][64 * D];
   __shared__ __align__(16) uint16_t Vs[2][64 * D];
   __shared__ float lwb[2][16];
 
@@ -143,12 +177,14 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   const int dc = lane % CPR;
   const int lane_off = (key * D + 8 * dc) * 2;
 
-  u32x4 kpre[SLOTS], vpre[SLOTS];
+  // K goes straight to LDS for gathered rows; dense rows stage it through
+  // registers like V (measured faster there)
+  u32x4 vpre[SLOTS], kpre[kGather ? 1 : SLOTS];
   int id_next = 0, id_far = 0;       // raw ids of chunks c+1 and c+2
   float lw_next = 0.f, lw_far = 0.f;
   float lw_store = 0.f;
 
-  auto issue_loads = [&](int c) {    // K/V of chunk c, from id_next
+  auto issue_loads = [&](int c) {    // V (dense: K and V) of chunk c, from id_next
     const bool ok = valid_id(c, id_next);
     const int idv = ok ? id_next : 0;
     lw_store = ok ? lw_next * kLog2e : -INFINITY;
@@ -165,21 +201,48 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
         soff = 0;
         voff = (sub ? id1 : id0) * BLOCK_BYTES + lane_off;
       }
-      kpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff, soff, 0));
+      if constexpr (!kGather)
+        kpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff, soff, 0));
       vpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, soff, 0));
     }
   };
-  auto store_chunk = [&](int buf) {
+  // K of chunk c (ids `raw`) straight into K stage buf: wave wv moves blocks
+  // 4wv..4wv+3, one direct load per 1 KB.  The block offset is in the per-lane
+  // offset, which the buffer range check covers.
+  auto issue_k = [&](int c, int raw, int stage) {
+    if constexpr (!kGather) return;
+    uint16_t* kst = Ks[stage];
+    const int idv = valid_id(c, raw) ? raw : 0;
+#pragma unroll
+    for (int j = 0; j < 4 / BPI; ++j) {
+      const int b0 = 4 * wv + BPI * j;
+      int idb = __builtin_amdgcn_readlane(idv, b0);
+      if constexpr (BPI == 2) {
+        const int id1 = __builtin_amdgcn_readlane(idv, b0 + 1);
+        idb = lane >= LPB ? id1 : idb;
+      }
+      const int b = b0 + lane / LPB;
+      const int rib = (lane % LPB) / CPR;
+      const int trow = 4 * b + rib;
+      const int voff = idb * BLOCK_BYTES + rib * D * 2 + (((lane % CPR) ^ (trow % CPR)) << 4);
+      buffer_load_lds16(krs, voff,
+                        (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(
+                            &kst[b0 * (BLOCK_BYTES / 2)]));
+    }
+  };
+  auto store_chunk = [&](int buf) {  // V of the chunk in registers, with its shifts
+    uint16_t* vst = Vs[buf];
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
       const int row = 4 * (4 * wv + i * BPS + sub) + key;
-      *reinterpret_cast<u32x4*>(&Ks[buf][row * KROW + 8 * dc]) = kpre[i];
+      if constexpr (!kGather)
+        *reinterpret_cast<u32x4*>(&Ks[buf][row * D + 8 * (dc ^ (row % CPR))]) = kpre[i];
       u32x4 hv;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         hv[e] = pack_f16_rtz(__uint_as_float(vpre[i][e] << 16),
                              __uint_as_float(vpre[i][e] & 0xffff0000u));
-      *reinterpret_cast<u32x4*>(&Vs[buf][row * D + 8 * (dc ^ vswz<D>(row))]) = hv;
+      *reinterpret_cast<u32x4*>(&vst[row * D + 8 * (dc ^ vswz<D>(row))]) = hv;
     }
     if (t < 16) lwb[buf][t] = lw_store;
   };
@@ -191,17 +254,18 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   float lsum0 = 0.f, lsum1 = 0.f;
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  // Pipeline: chunk c is computed from LDS stage c%2 while the registers carry
-  // chunk c+1 (loaded during the previous iteration) and the block ids of
-  // chunk c+2 are in flight.  At the top of iteration c the registers go to
-  // stage (c+1)%2 (free since the barrier that ended iteration c-1), then the
-  // loads of chunk c+2 are issued, so every gather load has a whole iteration
-  // to land.  Chunk indices are clamped to the last chunk so the prefetch code
-  // runs unconditionally (no branch merges that would force early waits); the
+  // Pipeline: chunk c is computed from LDS stage c%2.  At the top of
+  // iteration c the free stage (c+1)%2 receives K of chunk c+1 by direct
+  // loads (dense rows: from registers) and V of chunk c+1 from the registers
+  // (loaded during iteration c-1), then V of chunk c+2 is requested into the
+  // registers and the block ids of chunk c+3 are fetched.  The barrier that ends iteration c waits for all
+  // of it, so every load has a whole iteration to land.  Chunk indices are
+  // clamped to the last chunk so the prefetch code runs unconditionally; the
   // cost is a few redundant loads at the end.
   const int clast = nchunk > 0 ? nchunk - 1 : 0;
   if (nchunk > 0) {
     fetch_ids(0, id_next, lw_next);
+    issue_k(0, id_next, 0);
     issue_loads(0);
     fetch_ids(min(1, clast), id_far, lw_far);
     store_chunk(0);
@@ -210,18 +274,21 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     issue_loads(min(1, clast));
     fetch_ids(min(2, clast), id_far, lw_far);
   }
-  __syncthreads();
+  dma_barrier();
 
   // transpose-read geometry (per lane, fixed)
   const int tr_r = lane & 15;
   const int tr_g = (lane >> 4) & 1;
 
-  for (int c = 0; c < nchunk; ++c) {
-    const int buf = c & 1;
-    store_chunk(buf ^ 1);             // chunk c+1 (registers) -> free stage
+  auto step = [&](int c, int buf) {
+    const uint16_t* kst = Ks[buf];
+    const uint16_t* vst = Vs[buf];
+    // id_next holds the ids of chunk c+1 here
+    issue_k(min(c + 1, clast), id_next, buf ^ 1);  // K of chunk c+1 -> free stage
+    store_chunk(buf ^ 1);    // V of chunk c+1 (registers) -> free stage
     id_next = id_far;
     lw_next = lw_far;
-    issue_loads(min(c + 2, clast));   // chunk c+2 -> registers
+    issue_loads(min(c + 2, clast));   // V of chunk c+2 -> registers
     fetch_ids(min(c + 3, clast), id_far, lw_far);
 
     // S^T tile: lane holds query l32, keys 32*tt + 8*g + 4*hh + (0..3) = block 8tt+2g+hh
@@ -230,11 +297,20 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(&Ks[buf][(32 * tt + l32) * KROW + 16 * s + 8 * hh]);
+        const int krow = 32 * tt + l32;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            &kst[krow * D + (((2 * s + hh) ^ (krow % CPR)) << 3)]);
         sacc[tt] = mfma_bf16_32x32x16(a, qreg[s], sacc[tt]);
       }
     }
+    // keep four K operand reads in flight ahead of the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     if constexpr (!kGather) {
       if (c == nchunk - 1) {  // keys past N in the last dense chunk
         const int base = 64 * c;
@@ -299,8 +375,8 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
 #pragma unroll
         for (int u = 0; u < DT; ++u) {
           const int d0 = 32 * u + 16 * tr_g + 4 * (tr_r & 3);
-          const v4i16 va = lds_read_tr16(&Vs[buf][rowa * D + 8 * ((d0 >> 3) ^ vswz<D>(rowa)) + (d0 & 7)]);
-          const v4i16 vb = lds_read_tr16(&Vs[buf][rowb * D + 8 * ((d0 >> 3) ^ vswz<D>(rowb)) + (d0 & 7)]);
+          const v4i16 va = lds_read_tr16(&vst[rowa * D + 8 * ((d0 >> 3) ^ vswz<D>(rowa)) + (d0 & 7)]);
+          const v4i16 vb = lds_read_tr16(&vst[rowb * D + 8 * ((d0 >> 3) ^ vswz<D>(rowb)) + (d0 & 7)]);
           const f16x8 vop = __builtin_bit_cast(
               f16x8, u32x4{__builtin_bit_cast(u32x2, va)[0], __builtin_bit_cast(u32x2, va)[1],
                            __builtin_bit_cast(u32x2, vb)[0], __builtin_bit_cast(u32x2, vb)[1]});
@@ -308,7 +384,17 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
         }
       }
     }
-    __syncthreads();
+    dma_barrier();
+  };
+  if constexpr (kGather) {
+    // unrolled by two so that stage addresses are constants (measured faster
+    // for the gathered rows, slower for the dense ones)
+    for (int c = 0; c < nchunk; c += 2) {
+      step(c, 0);
+      if (c + 1 < nchunk) step(c + 1, 1);
+    }
+  } else {
+    for (int c = 0; c < nchunk; ++c) step(c, c & 1);
   }
 
   // epilogue: O^T lane layout = query l32, dims 32u + 8g + 4hh + (0..3)
