@@ -333,7 +333,8 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
         mloc = fmaxf(mloc, fmaf(gm, scale_log2, lwg[4 * tt + g]));
       }
     }
-    const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const f32x2 mp = pair_x32(mloc);
+    const float mrow = fmaxf(mp[0], mp[1]);
     const bool need = mrow > m_used + kRescaleLog2;
     if (__any(need)) {
       const float alpha = need ? __builtin_amdgcn_exp2f(m_used - mrow) : 1.f;
@@ -399,7 +400,8 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
 
   // epilogue: O^T lane layout = query l32, dims 32u + 8g + 4hh + (0..3)
   const float lsum = lsum0 + lsum1;
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const f32x2 lp = pair_x32(lsum);
+  const float ltot = lp[0] + lp[1];
   if (qrow < N) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     uint16_t* orow = O + (bh * N + qrow) * D;

@@ -65,6 +65,36 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return x * q + (x < rem ? x : rem) + k;
 }
 
+// Exchanges between lane groups through the register file (gfx950
+// v_permlane32_swap / v_permlane16_swap) in place of LDS-routed shuffles.
+// permlane32_swap(a, b) returns {a of lanes 0-31 | b of lanes 0-31} and
+// {a of lanes 32-63 | b of lanes 32-63} (in the lower | upper half), so with
+// a = b = v every lane receives v of lanes l & ~32 and l | 32, in that order;
+// permlane16_swap does the same for the 16-lane rows 0,1 and 2,3.  Results
+// are identical in both lanes of a pair, which keeps pairwise sums in the same
+// order everywhere.
+__device__ __forceinline__ f32x2 pair_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ f32x2 pair_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ int sum_x32(int v) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  return (int)(r[0] + r[1]);
+}
+__device__ __forceinline__ int sum_x16(int v) {
+  const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+  return (int)(r[0] + r[1]);
+}
+// {a, b} -> lower half gets a of both halves, upper half gets b of both halves
+__device__ __forceinline__ f32x2 cross_x32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -253,8 +253,12 @@ __global__ __launch_bounds__(256) void k_kmeans_mfma(const uint16_t* __restrict_
       *reinterpret_cast<u32x2*>(planes + 16 * XS + e) = u32x2{mw[0], mw[1]};
       *reinterpret_cast<u32x2*>(planes + 32 * XS + e) = u32x2{lw[0], lw[1]};
     }
-    sq += __shfl_xor(sq, 16);
-    sq += __shfl_xor(sq, 32);
+    {
+      const f32x2 r16 = pair_x16(sq);
+      sq = r16[0] + r16[1];
+      const f32x2 r32 = pair_x32(sq);
+      sq = r32[0] + r32[1];
+    }
     if (g == 0) npart[w][i] = sq;
   };
   publish();
@@ -288,15 +292,16 @@ __global__ __launch_bounds__(256) void k_kmeans_mfma(const uint16_t* __restrict_
           a = 4 * g + v;
         }
       }
-#pragma unroll
-      for (int o = 16; o < (C > 8 ? 64 : 32); o <<= 1) {
-        const float ob = __shfl_xor(best, o);
-        const int oa = __shfl_xor(a, o);
-        if (ob < best || (ob == best && oa < a)) {
-          best = ob;
-          a = oa;
-        }
-      }
+      // lexicographic minimum of (distance, index) over the lane pairs l, l^16
+      // (and l^32 for 16 clusters)
+      auto pick = [&](const f32x2& b2, const f32x2& a2) {
+        const int a0 = __float_as_int(a2[0]), a1 = __float_as_int(a2[1]);
+        const bool hi = b2[1] < b2[0] || (b2[1] == b2[0] && a1 < a0);
+        best = hi ? b2[1] : b2[0];
+        a = hi ? a1 : a0;
+      };
+      pick(pair_x16(best), pair_x16(__int_as_float(a)));
+      if constexpr (C > 8) pick(pair_x32(best), pair_x32(__int_as_float(a)));
       // one-hot column of point p (rows c >= C and points p >= n stay zero)
       const int p = 32 * w + 16 * u + i;
       if (4 * g < C && p < n) {
@@ -319,8 +324,7 @@ __global__ __launch_bounds__(256) void k_kmeans_mfma(const uint16_t* __restrict_
 #pragma unroll
       for (int u = 0; u < UT; ++u) sum[u] = mfma_bf16_16x16x32(ub[u][ks], B, sum[u]);
     }
-    cnt += __shfl_xor(cnt, 16);
-    cnt += __shfl_xor(cnt, 32);  // members of cluster i
+    cnt = sum_x32(sum_x16(cnt));  // members of cluster i
     if (cnt > 0) {
       // quotient sum / cnt: reciprocal estimate plus one residual correction
       const float fc = (float)cnt;

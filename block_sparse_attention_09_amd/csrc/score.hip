@@ -197,7 +197,8 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
       float tmax = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, x[v]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // finite: every tile has a valid key
+      const f32x2 tp = pair_x32(tmax);
+      tmax = fmaxf(tp[0], tp[1]);  // finite: every tile has a valid key
       const float m_new = fmaxf(m_run, tmax);
       s_run *= __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -206,7 +207,10 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
     };
     run_pass(hbase, lbase, mma1, fix1, epi1);
   }
-  s_run += __shfl_xor(s_run, 32);
+  {
+    const f32x2 sp = pair_x32(s_run);
+    s_run = sp[0] + sp[1];
+  }
   // log2 of (w_c / normaliser); -inf for an empty cluster
   const float a_c = log2f(wc) - (m_run + log2f(s_run));
   if (hh == 0) a_lds[crow] = a_c;
@@ -250,28 +254,28 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
     const int key = 32 * tile + l32;
     if constexpr (C == 8) {
       // rows 8g..8g+7 of the wave = one query block; this half holds 4 of them
-      float tot[4];
+      float part[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float part = (p[4 * g] + p[4 * g + 1]) + (p[4 * g + 2] + p[4 * g + 3]);
-        tot[g] = part + __shfl_xor(part, 32);
-      }
+      for (int g = 0; g < 4; ++g)
+        part[g] = (p[4 * g] + p[4 * g + 1]) + (p[4 * g + 2] + p[4 * g + 3]);
+      // the lower half completes blocks 2 and 3, the upper half blocks 0 and 1
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
-        const int g = 2 * hh + gg;
-        put(4 * wv + g, key, tot[g]);
+        const f32x2 r = cross_x32(part[2 + gg], part[gg]);
+        put(4 * wv + (hh ? gg : 2 + gg), key, r[0] + r[1]);
       }
     } else {
       // C == 16: rows 16gp..16gp+15 = one query block
-      float tot[2];
+      float part[2];
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
-        float part = 0.f;
+        part[gp] = 0.f;
 #pragma unroll
-        for (int v = 8 * gp; v < 8 * gp + 8; ++v) part += p[v];
-        tot[gp] = part + __shfl_xor(part, 32);
+        for (int v = 8 * gp; v < 8 * gp + 8; ++v) part[gp] += p[v];
       }
-      put(2 * wv + hh, key, tot[hh]);
+      // the lower half completes block 1, the upper half block 0
+      const f32x2 r = cross_x32(part[1], part[0]);
+      put(2 * wv + (hh ? 0 : 1), key, r[0] + r[1]);
     }
   };
   run_pass(hbase, lbase, mma2, fix2, epi2);
