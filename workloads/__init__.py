@@ -57,6 +57,8 @@ class Workload:
     plan_seed: int = 0                  # sampler seed
     plan_reuse: int = 1                 # calls that share one plan
     drift: float = 0.0                  # per-call q/k drift std when reused
+    pe_amp: float = 1.0                 # amplitude of the position code (1 everywhere
+                                        # except the plan-quality sweep)
 
     @property
     def N(self) -> int:
@@ -141,7 +143,7 @@ class Generator:
     def __init__(self, wl: Workload, heads: Optional[List[Tuple[int, int]]] = None):
         self.wl = wl
         self.rng = np.random.default_rng(wl.seed)
-        self.pe = position_code(wl.grid, wl.D).astype(np.float32)
+        self.pe = (wl.pe_amp * position_code(wl.grid, wl.D)).astype(np.float32)
 
     def _one(self) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
         wl = self.wl
