@@ -34,7 +34,8 @@ from workloads import CONFIGS, Generator, Workload  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0         # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0
-PAIR_FLOP = lambda D: 4 * 128 * 4 * D   # one (query block, key block) pair: QK^T + PV
+# one (query block, key block) pair of kb keys: QK^T + PV over 128 queries
+PAIR_FLOP = lambda D, kb=4: 4 * 128 * kb * D
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
 
 
@@ -74,7 +75,7 @@ def cpu_baseline(wl: Workload, budget: float, dense_flop_per_head: float):
         threads = 1
     from workloads import make_qkv
     q, k, v = make_qkv(wl, heads=1)
-    op = oracle.Problem(B=1, H=1, N=wl.N, D=wl.D, n_clusters=wl.n_clusters,
+    op = oracle.Problem(B=1, H=1, N=wl.N, D=wl.D, kv_block=wl.kv_block, n_clusters=wl.n_clusters,
                         kmeans_iters=wl.kmeans_iters, n_forced_tail=wl.n_text)
     rows = list(range(op.R))
     t0 = time.perf_counter()
@@ -125,6 +126,10 @@ def main():
                          "Infinity Cache; reported as a median (0 skips)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--kv-block", type=int, default=4,
+                    help="key/value block size (a power of two from 4 to 128)")
+    ap.add_argument("--grid", default=None,
+                    help="T,H,W latent grid in place of the workload's (block-size sweep)")
     ap.add_argument("--probe", choices=["copy"], default=None)
     args = ap.parse_args()
 
@@ -142,6 +147,11 @@ def main():
         return
 
     wl = CONFIGS[args.workload]
+    if args.grid:
+        wl = wl.scaled(grid=tuple(int(x) for x in args.grid.split(",")))
+    if args.kv_block != wl.kv_block:
+        wl = wl.scaled(kv_block=args.kv_block)
+    stock = wl == CONFIGS[args.workload]
     budget = args.budget if args.budget is not None else \
         (0.10 if 0.10 in wl.budgets else wl.budgets[0])
     if budget >= 1.0:
@@ -152,7 +162,7 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s")
 
-    prob = ab.Problem(wl.B, wl.H, wl.N, wl.D, n_clusters=wl.n_clusters,
+    prob = ab.Problem(wl.B, wl.H, wl.N, wl.D, kv_block=wl.kv_block, n_clusters=wl.n_clusters,
                       kmeans_iters=wl.kmeans_iters, n_forced_tail=wl.n_text, dtype=wl.dtype)
     ws = ab.workspace(prob, q.device)
     pl = ab.empty_plan(prob, ab.nnz_bound(prob, budget), q.device)
@@ -216,13 +226,14 @@ def main():
         log(f"attend from a cold cache: median {attend_cold_ms:.3f} ms over {args.cold_reps} reps")
 
     # per-row counts of the timed plan: computed tiles include the padding of
-    # each row's last 16-block chunk; useful work excludes the padded query rows
+    # each row's last 64-key chunk; useful work excludes the padded query rows
     # of a head's last query block
+    kb = wl.kv_block
     rp = pl.row_ptr.cpu().numpy().astype(np.int64)
     row_nnz = np.diff(rp)
     valid_q = np.minimum(128, wl.N - 128 * (np.arange(prob.R) % prob.n_qb))
-    executed_pairs = int((np.ceil(row_nnz / 16.0) * 16).sum())
-    useful_flop = float((row_nnz * valid_q).sum()) * 4 * 4 * wl.D
+    executed_keys = int((np.ceil(row_nnz * kb / 64.0) * 64).sum())
+    useful_flop = float((row_nnz * valid_q).sum()) * 4 * kb * wl.D
 
     dense_ms = None
     if not args.no_dense:
@@ -241,14 +252,15 @@ def main():
 
     B, H, N, D = wl.B, wl.H, wl.N, wl.D
     dense_flop = 4.0 * B * H * N * N * D
-    attend_flop = PAIR_FLOP(D) * nnz
+    attend_flop = PAIR_FLOP(D, kb) * nnz
     achieved = attend_flop / (attend_ms * 1e-3) / 1e12
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         t = json.load(open(TRAFFIC_FILE))
         if t.get("attend_src_sha") == src_sha(os.path.join(
                 ROOT, "block_sparse_attention_09_amd", "csrc", "attend.hip")) \
-                and t.get("workload") == wl.name and abs(t.get("budget", -1) - budget) < 1e-9:
+                and stock and t.get("workload") == wl.name \
+                and abs(t.get("budget", -1) - budget) < 1e-9:
             traffic = t.get("bytes_per_launch")
 
     out = {
@@ -267,7 +279,8 @@ def main():
         "config": {
             "workload": f"{wl.name}: B={B} H={H} N={N} ({'x'.join(map(str, wl.grid))}"
                         f"{' + %d text' % wl.n_text if wl.n_text else ''}) D={D} {wl.dtype}, "
-                        f"budget {budget}, {wl.n_clusters} clusters, q block 128, kv block 4",
+                        f"budget {budget}, {wl.n_clusters} clusters, q block 128, "
+                        f"kv block {wl.kv_block}",
             "budget": budget,
             "plan_rows": prob.R,
             "nnz": nnz,
@@ -294,8 +307,8 @@ def main():
             "dense_mfma_frac": (dense_flop / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if dense_ms else None,
             "attend_flop_per_launch": attend_flop,
             "attend_ms_cold_median": attend_cold_ms,
-            "attend_mfma_frac_executed_tiles": PAIR_FLOP(D) * executed_pairs / (attend_ms * 1e-3) / 1e12
-                                              / PEAK_BF16_TFLOPS,
+            "attend_mfma_frac_executed_tiles": PAIR_FLOP(D, 1) * executed_keys / (attend_ms * 1e-3)
+                                              / 1e12 / PEAK_BF16_TFLOPS,
             "attend_mfma_frac_useful": useful_flop / (attend_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             # algorithmic selector traffic: Q and K read, S written once and read
             # twice (4 + 8 bytes per pair), the plan written

@@ -30,7 +30,10 @@ abatt_status make_shape(const abatt_problem_t* p, Shape* s) {
   if (p->n_clusters > p->q_block) return ABATT_EINVAL;
   // what the kernels implement
   if (p->D != 64 && p->D != 128) return ABATT_EUNSUPPORTED;
-  if (p->q_block != 128 || p->kv_block != 4) return ABATT_EUNSUPPORTED;
+  if (p->q_block != 128) return ABATT_EUNSUPPORTED;
+  // key blocks: a power of two from 4 to 128 tokens
+  if (p->kv_block < 4 || p->kv_block > 128 || (p->kv_block & (p->kv_block - 1)) != 0)
+    return ABATT_EUNSUPPORTED;
   if (p->n_clusters != 8 && p->n_clusters != 16) return ABATT_EUNSUPPORTED;
   const int64_t n_qb = (p->N + p->q_block - 1) / p->q_block;
   const int64_t R = (int64_t)p->B * p->H * n_qb;

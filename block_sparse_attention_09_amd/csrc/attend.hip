@@ -100,15 +100,15 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const float* __restrict__ logw, int64_t capacity,
     const int32_t* __restrict__ status, uint16_t* __restrict__ O, float* __restrict__ lse, int N,
-    int n_qb, int n_kb, int R, float scale_log2) {
+    int n_qb, int n_kb, int R, float scale_log2, int lkb) {
   constexpr int KS = D / 16;          // QK^T k-steps
   constexpr int DT = D / 32;          // PV output tiles
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int SLOTS = 2 * D / 64;   // 16-byte loads per lane per chunk, for K and for V
-  constexpr int BPS = 64 / (4 * CPR); // blocks covered by one slot of a wave (1 or 2)
-  constexpr int BLOCK_BYTES = 4 * D * 2;
-  constexpr int LPB = BLOCK_BYTES / 16;  // lanes of one direct K load per block (64 or 32)
-  constexpr int BPI = 64 / LPB;          // blocks per direct K load (1 or 2)
+  constexpr int BPS = 64 / (4 * CPR); // 4-key groups covered by one slot of a wave (1 or 2)
+  constexpr int GROUP_BYTES = 4 * D * 2;  // one group of 4 keys
+  constexpr int LPB = GROUP_BYTES / 16;   // lanes of one direct K load per group (64 or 32)
+  constexpr int BPI = 64 / LPB;           // groups per direct K load (1 or 2)
   // K tile: row-major, 16-byte slot s of row r stored at s ^ (r % CPR)
   // (conflict-free operand reads without padding; the direct loads place each
   // lane's 16 bytes at a fixed LDS position, so the swizzle is chosen through
@@ -138,7 +138,9 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   } else {
     nblk = (N + 3) / 4;
   }
-  const int nchunk = (nblk + 15) / 16;
+  // keys of the row: nblk blocks of 2^lkb tokens (dense rows: 4-token groups)
+  const int nchunk = (int)((((int64_t)nblk << lkb) + 63) / 64);
+  const int kbmask = (1 << lkb) - 1;
 
   const __amdgpu_buffer_rsrc_t krs = head_rsrc(K + bh * N * D, N * D * 2);
   const __amdgpu_buffer_rsrc_t vrs = head_rsrc(V + bh * N * D, N * D * 2);
@@ -153,9 +155,14 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
       qreg[s] = bf16x8{};
   }
 
-  // block ids of a chunk: lane j holds block 16c + (j & 15), branch-free
+  // A chunk is 64 consecutive keys of the row's key sequence, 16 groups of 4;
+  // group g of chunk c starts at key 64c + 4g, in block (64c + 4g) >> lkb at
+  // token (64c + 4g) & kbmask of the block.  Lane j holds the block id and
+  // shift of group j & 15 (repeated for blocks longer than 4), branch-free.
+  auto group_block = [&](int c, int g) { return (64 * c + 4 * g) >> lkb; };
+  auto group_token = [&](int c, int g) { return (64 * c + 4 * g) & kbmask; };
   auto fetch_ids = [&](int c, int& id, float& lw) {
-    const int idx = 16 * c + (lane & 15);
+    const int idx = group_block(c, lane & 15);
     if constexpr (kGather) {
       const int64_t at = start + (idx < nblk ? idx : nblk - 1);
       id = col_idx[at];
@@ -167,15 +174,16 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   };
   // validity is applied when the ids are used (keeps the loads in flight)
   auto valid_id = [&](int c, int raw) -> bool {
-    if constexpr (kGather) return 16 * c + (lane & 15) < nblk && raw >= 0 && raw < n_kb;
+    if constexpr (kGather) return group_block(c, lane & 15) < nblk && raw >= 0 && raw < n_kb;
     return true;
   };
 
-  // lane -> (block within the slot, key within the block, 16-byte chunk)
+  // lane -> (group within the slot, key within the group, 16-byte chunk)
   const int sub = lane / (4 * CPR);
   const int key = (lane % (4 * CPR)) / CPR;
   const int dc = lane % CPR;
   const int lane_off = (key * D + 8 * dc) * 2;
+  constexpr int ROW_BYTES = D * 2;
 
   // K goes straight to LDS for gathered rows; dense rows stage it through
   // registers like V (measured faster there)
@@ -184,30 +192,31 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   float lw_next = 0.f, lw_far = 0.f;
   float lw_store = 0.f;
 
+  // The whole row offset goes in the per-lane offset, which the buffer range
+  // check covers: rows past N (the dense path's last partial group) read zero.
   auto issue_loads = [&](int c) {    // V (dense: K and V) of chunk c, from id_next
     const bool ok = valid_id(c, id_next);
     const int idv = ok ? id_next : 0;
     lw_store = ok ? lw_next * kLog2e : -INFINITY;
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
-      const int bi = 4 * wv + i * BPS;
-      int voff, soff;
+      const int g0 = 4 * wv + i * BPS;
+      int row0;                       // first row of this lane's group
       if constexpr (BPS == 1) {
-        soff = __builtin_amdgcn_readlane(idv, bi) * BLOCK_BYTES;
-        voff = lane_off;
+        row0 = (__builtin_amdgcn_readlane(idv, g0) << lkb) + group_token(c, g0);
       } else {
-        const int id0 = __builtin_amdgcn_readlane(idv, bi);
-        const int id1 = __builtin_amdgcn_readlane(idv, bi + 1);
-        soff = 0;
-        voff = (sub ? id1 : id0) * BLOCK_BYTES + lane_off;
+        const int r0 = (__builtin_amdgcn_readlane(idv, g0) << lkb) + group_token(c, g0);
+        const int r1 = (__builtin_amdgcn_readlane(idv, g0 + 1) << lkb) + group_token(c, g0 + 1);
+        row0 = sub ? r1 : r0;
       }
+      const int voff = row0 * ROW_BYTES + lane_off;
       if constexpr (!kGather)
-        kpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff, soff, 0));
-      vpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, soff, 0));
+        kpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff, 0, 0));
+      vpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, 0, 0));
     }
   };
-  // K of chunk c (ids `raw`) straight into K stage buf: wave wv moves blocks
-  // 4wv..4wv+3, one direct load per 1 KB.  The block offset is in the per-lane
+  // K of chunk c (ids `raw`) straight into K stage buf: wave wv moves groups
+  // 4wv..4wv+3, one direct load per 1 KB.  The row offset is in the per-lane
   // offset, which the buffer range check covers.
   auto issue_k = [&](int c, int raw, int stage) {
     if constexpr (!kGather) return;
@@ -216,18 +225,18 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
 #pragma unroll
     for (int j = 0; j < 4 / BPI; ++j) {
       const int b0 = 4 * wv + BPI * j;
-      int idb = __builtin_amdgcn_readlane(idv, b0);
+      int row0 = (__builtin_amdgcn_readlane(idv, b0) << lkb) + group_token(c, b0);
       if constexpr (BPI == 2) {
-        const int id1 = __builtin_amdgcn_readlane(idv, b0 + 1);
-        idb = lane >= LPB ? id1 : idb;
+        const int r1 = (__builtin_amdgcn_readlane(idv, b0 + 1) << lkb) + group_token(c, b0 + 1);
+        row0 = lane >= LPB ? r1 : row0;
       }
       const int b = b0 + lane / LPB;
       const int rib = (lane % LPB) / CPR;
       const int trow = 4 * b + rib;
-      const int voff = idb * BLOCK_BYTES + rib * D * 2 + (((lane % CPR) ^ (trow % CPR)) << 4);
+      const int voff = (row0 + rib) * ROW_BYTES + (((lane % CPR) ^ (trow % CPR)) << 4);
       buffer_load_lds16(krs, voff,
                         (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(
-                            &kst[b0 * (BLOCK_BYTES / 2)]));
+                            &kst[b0 * (GROUP_BYTES / 2)]));
     }
   };
   auto store_chunk = [&](int buf) {  // V of the chunk in registers, with its shifts
@@ -430,8 +439,8 @@ __global__ __launch_bounds__(128) void k_attend_f32(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const float* __restrict__ logw, int64_t capacity, const int32_t* __restrict__ status,
     float* __restrict__ O, float* __restrict__ lse, int N, int n_qb, int n_kb, int R,
-    float scale_log2) {
-  constexpr int CK = 32;  // keys per chunk = 8 blocks
+    float scale_log2, int lkb) {
+  constexpr int CK = 32;  // keys per chunk
   __shared__ __align__(16) float Kf[CK * D];
   __shared__ __align__(16) float Vf[CK * D];
   __shared__ float lwk[CK];
@@ -452,7 +461,9 @@ __global__ __launch_bounds__(128) void k_attend_f32(
   } else {
     nblk = (N + 3) / 4;
   }
-  const int nchunk = (nblk + 7) / 8;
+  // key kap of the row's key sequence: block kap >> lkb, token kap & kbmask
+  const int nchunk = (int)((((int64_t)nblk << lkb) + CK - 1) / CK);
+  const int kbmask = (1 << lkb) - 1;
   const float* Kh = K + bh * N * D;
   const float* Vh = V + bh * N * D;
 
@@ -468,7 +479,8 @@ __global__ __launch_bounds__(128) void k_attend_f32(
     __syncthreads();
     for (int i = t; i < CK * D / 4; i += 128) {
       const int key = (4 * i) / D, e = (4 * i) % D;
-      const int idx = c * 8 + key / 4;
+      const int kap = c * CK + key;
+      const int idx = kap >> lkb;
       int id = 0;
       float lw = -INFINITY;
       if constexpr (kGather) {
@@ -481,9 +493,9 @@ __global__ __launch_bounds__(128) void k_attend_f32(
         }
       } else {
         id = idx;
-        lw = (4 * idx + (key & 3) < N) ? 0.f : -INFINITY;
+        lw = kap < N ? 0.f : -INFINITY;
       }
-      int64_t tok = 4 * (int64_t)id + (key & 3);
+      int64_t tok = ((int64_t)id << lkb) + (kap & kbmask);
       if (tok >= N) tok = N - 1;
       *reinterpret_cast<f32x4*>(&Kf[key * D + e]) = *reinterpret_cast<const f32x4*>(Kh + tok * D + e);
       *reinterpret_cast<f32x4*>(&Vf[key * D + e]) = *reinterpret_cast<const f32x4*>(Vh + tok * D + e);
@@ -543,14 +555,18 @@ static void launch_attend_t(const Shape& s, const void* Q, const void* K, const 
                             int64_t capacity, const int32_t* status, void* O, float* lse,
                             hipStream_t st) {
   const float sl2 = s.scale * kLog2e;
+  // gathered rows use the problem's key-block size; dense rows run in groups of 4
+  int lkb = 2;
+  if (kGather)
+    while ((1 << lkb) < s.kv_block) ++lkb;
   if (s.bf16) {
     k_attend_bf16<D, kGather><<<s.R, 256, 0, st>>>(
         (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, row_ptr, col_idx, logw,
-        capacity, status, (uint16_t*)O, lse, s.N, s.n_qb, s.n_kb, s.R, sl2);
+        capacity, status, (uint16_t*)O, lse, s.N, s.n_qb, s.n_kb, s.R, sl2, lkb);
   } else {
     k_attend_f32<D, kGather><<<s.R, 128, 0, st>>>(
         (const float*)Q, (const float*)K, (const float*)V, row_ptr, col_idx, logw, capacity,
-        status, (float*)O, lse, s.N, s.n_qb, s.n_kb, s.R, sl2);
+        status, (float*)O, lse, s.N, s.n_qb, s.n_kb, s.R, sl2, lkb);
   }
 }
 

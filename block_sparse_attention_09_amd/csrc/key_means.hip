@@ -1,10 +1,12 @@
-// Mean key of every sparse 4-token key block.
+// Mean key of every sparse key block (4 consecutive tokens by default).
 //
 // [hamidun] "AB-Attention's three techniques", IBCS paragraph: key blocks are
 // scored through their averaged keys; the third technique fixes the key block
-// at 4 consecutive tokens.  HBM-bound: each block's 4 rows are read once
-// (16-byte lane loads, consecutive lanes on consecutive bytes) and one fp32
-// row is written.
+// at 4 consecutive tokens (and compares it with 128).  HBM-bound: each block's
+// rows are read once (16-byte lane loads, consecutive lanes on consecutive
+// bytes) and one fp32 row is written.  Blocks of kb > 4 tokens are summed in
+// token order, like the 4-token form, then scaled by 1/kb (exact, kb a power
+// of two).
 #include "common.h"
 #include "kernels.h"
 
@@ -17,7 +19,8 @@ namespace abatt {
 template <int D, bool kSplit>
 __global__ __launch_bounds__(256) void k_key_means_bf16(const uint16_t* __restrict__ K,
                                                         float* __restrict__ kmean,
-                                                        int64_t total, int N, int n_kbs) {
+                                                        int64_t total, int N, int n_kbs,
+                                                        int kb) {
   constexpr int CH = D / 8;  // 16-byte chunks per row
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
@@ -25,20 +28,35 @@ __global__ __launch_bounds__(256) void k_key_means_bf16(const uint16_t* __restri
     const int64_t bj = i / CH;  // bh * n_kbs + j
     const int j = (int)(bj % n_kbs);
     const int64_t bh = bj / n_kbs;
-    const uint16_t* src = K + (bh * N + 4 * (int64_t)j) * D + 8 * c;
-    u32x4 r0 = *reinterpret_cast<const u32x4*>(src);
-    u32x4 r1 = *reinterpret_cast<const u32x4*>(src + D);
-    u32x4 r2 = *reinterpret_cast<const u32x4*>(src + 2 * D);
-    u32x4 r3 = *reinterpret_cast<const u32x4*>(src + 3 * D);
+    const uint16_t* src = K + (bh * N + (int64_t)kb * j) * D + 8 * c;
     float out[8];
+    if (kb == 4) {
+      u32x4 r0 = *reinterpret_cast<const u32x4*>(src);
+      u32x4 r1 = *reinterpret_cast<const u32x4*>(src + D);
+      u32x4 r2 = *reinterpret_cast<const u32x4*>(src + 2 * D);
+      u32x4 r3 = *reinterpret_cast<const u32x4*>(src + 3 * D);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a0 = bf16_bits_to_f32(r0[e] & 0xffffu), b0 = bf16_bits_to_f32(r0[e] >> 16);
-      const float a1 = bf16_bits_to_f32(r1[e] & 0xffffu), b1 = bf16_bits_to_f32(r1[e] >> 16);
-      const float a2 = bf16_bits_to_f32(r2[e] & 0xffffu), b2 = bf16_bits_to_f32(r2[e] >> 16);
-      const float a3 = bf16_bits_to_f32(r3[e] & 0xffffu), b3 = bf16_bits_to_f32(r3[e] >> 16);
-      out[2 * e] = (((a0 + a1) + a2) + a3) * 0.25f;
-      out[2 * e + 1] = (((b0 + b1) + b2) + b3) * 0.25f;
+      for (int e = 0; e < 4; ++e) {
+        const float a0 = bf16_bits_to_f32(r0[e] & 0xffffu), b0 = bf16_bits_to_f32(r0[e] >> 16);
+        const float a1 = bf16_bits_to_f32(r1[e] & 0xffffu), b1 = bf16_bits_to_f32(r1[e] >> 16);
+        const float a2 = bf16_bits_to_f32(r2[e] & 0xffffu), b2 = bf16_bits_to_f32(r2[e] >> 16);
+        const float a3 = bf16_bits_to_f32(r3[e] & 0xffffu), b3 = bf16_bits_to_f32(r3[e] >> 16);
+        out[2 * e] = (((a0 + a1) + a2) + a3) * 0.25f;
+        out[2 * e + 1] = (((b0 + b1) + b2) + b3) * 0.25f;
+      }
+    } else {
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int tk = 0; tk < kb; ++tk) {
+        const u32x4 rr = *reinterpret_cast<const u32x4*>(src + (int64_t)tk * D);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bf16_bits_to_f32(rr[e] & 0xffffu);
+          acc[2 * e + 1] += bf16_bits_to_f32(rr[e] >> 16);
+        }
+      }
+      const float inv = 1.f / (float)kb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = acc[e] * inv;
     }
     if constexpr (kSplit) {
       uint16_t* hi = reinterpret_cast<uint16_t*>(kmean);
@@ -66,7 +84,8 @@ __global__ __launch_bounds__(256) void k_key_means_bf16(const uint16_t* __restri
 template <int D, bool kSplit>
 __global__ __launch_bounds__(256) void k_key_means_f32(const float* __restrict__ K,
                                                        float* __restrict__ kmean,
-                                                       int64_t total, int N, int n_kbs) {
+                                                       int64_t total, int N, int n_kbs,
+                                                       int kb) {
   constexpr int CH = D / 4;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
@@ -74,14 +93,26 @@ __global__ __launch_bounds__(256) void k_key_means_f32(const float* __restrict__
     const int64_t bj = i / CH;
     const int j = (int)(bj % n_kbs);
     const int64_t bh = bj / n_kbs;
-    const float* src = K + (bh * N + 4 * (int64_t)j) * D + 4 * c;
-    f32x4 r0 = *reinterpret_cast<const f32x4*>(src);
-    f32x4 r1 = *reinterpret_cast<const f32x4*>(src + D);
-    f32x4 r2 = *reinterpret_cast<const f32x4*>(src + 2 * D);
-    f32x4 r3 = *reinterpret_cast<const f32x4*>(src + 3 * D);
+    const float* src = K + (bh * N + (int64_t)kb * j) * D + 4 * c;
     f32x4 o;
+    if (kb == 4) {
+      f32x4 r0 = *reinterpret_cast<const f32x4*>(src);
+      f32x4 r1 = *reinterpret_cast<const f32x4*>(src + D);
+      f32x4 r2 = *reinterpret_cast<const f32x4*>(src + 2 * D);
+      f32x4 r3 = *reinterpret_cast<const f32x4*>(src + 3 * D);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = (((r0[e] + r1[e]) + r2[e]) + r3[e]) * 0.25f;
+      for (int e = 0; e < 4; ++e) o[e] = (((r0[e] + r1[e]) + r2[e]) + r3[e]) * 0.25f;
+    } else {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int tk = 0; tk < kb; ++tk) {
+        const f32x4 rr = *reinterpret_cast<const f32x4*>(src + (int64_t)tk * D);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += rr[e];
+      }
+      const float inv = 1.f / (float)kb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = acc[e] * inv;
+    }
     if constexpr (kSplit) {
       uint16_t* hi = reinterpret_cast<uint16_t*>(kmean);
       uint16_t* lo = hi + total * 4;
@@ -107,14 +138,18 @@ static hipError_t launch_means(const Shape& s, const void* K, float* out, hipStr
   const int grid = (int)(want < 65536 ? want : 65536);
   if (s.bf16) {
     if (s.D == 128)
-      k_key_means_bf16<128, kSplit><<<grid, 256, 0, st>>>((const uint16_t*)K, out, total, s.N, s.n_kbs);
+      k_key_means_bf16<128, kSplit><<<grid, 256, 0, st>>>((const uint16_t*)K, out, total, s.N, s.n_kbs,
+                                                         s.kv_block);
     else
-      k_key_means_bf16<64, kSplit><<<grid, 256, 0, st>>>((const uint16_t*)K, out, total, s.N, s.n_kbs);
+      k_key_means_bf16<64, kSplit><<<grid, 256, 0, st>>>((const uint16_t*)K, out, total, s.N, s.n_kbs,
+                                                         s.kv_block);
   } else {
     if (s.D == 128)
-      k_key_means_f32<128, kSplit><<<grid, 256, 0, st>>>((const float*)K, out, total, s.N, s.n_kbs);
+      k_key_means_f32<128, kSplit><<<grid, 256, 0, st>>>((const float*)K, out, total, s.N, s.n_kbs,
+                                                        s.kv_block);
     else
-      k_key_means_f32<64, kSplit><<<grid, 256, 0, st>>>((const float*)K, out, total, s.N, s.n_kbs);
+      k_key_means_f32<64, kSplit><<<grid, 256, 0, st>>>((const float*)K, out, total, s.N, s.n_kbs,
+                                                        s.kv_block);
   }
   return hipGetLastError();
 }

@@ -64,7 +64,8 @@ typedef enum { ABATT_F32 = 0, ABATT_BF16 = 1 } abatt_dtype;
 typedef struct {
   int32_t B, H, N, D;       /* batch, heads, tokens, head dim; D in {64, 128}          */
   int32_t q_block;          /* query block size; the kernels implement 128             */
-  int32_t kv_block;         /* key/value block size; the kernels implement 4           */
+  int32_t kv_block;         /* key/value block size: 4 (the pages' choice) or another  */
+                            /* power of two up to 128; dense attention ignores it     */
   int32_t n_clusters;       /* k-means clusters per query block: 8 or 16               */
   int32_t kmeans_iters;     /* Lloyd iterations, >= 1                                  */
   int32_t n_forced_tail;    /* trailing tokens kept in every row; multiple of kv_block */

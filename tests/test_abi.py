@@ -59,7 +59,8 @@ def test_sizes(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(D=96), -2), (dict(n_clusters=4), -2), (dict(q_block=64), -2),
-    (dict(kv_block=8), -2), (dict(N=0), -1), (dict(H=0), -1), (dict(N=1022), -1),
+    (dict(kv_block=256), -2), (dict(kv_block=2), -2), (dict(kv_block=12, N=1020), -2),
+    (dict(kv_block=16, N=1032), -1), (dict(N=0), -1), (dict(H=0), -1), (dict(N=1022), -1),
     (dict(n_forced_tail=6), -1), (dict(scale=-1.0), -1), (dict(kmeans_iters=0), -1),
 ])
 def test_bad_problems(lib, kw, code):
@@ -71,6 +72,15 @@ def test_bad_problems(lib, kw, code):
     r = lib.abatt_plan(ctypes.byref(p.c()), fake, fake, 0.1, 0, fake, 1 << 40,
                        ctypes.byref(pl), None)
     assert r == code
+
+
+@pytest.mark.parametrize("kb", [4, 8, 16, 32, 64, 128])
+def test_key_block_sizes(lib, kb):
+    # powers of two from 4 to 128 tokens; blocks and forced blocks scale with kb
+    p = prob(N=2048 + 2 * kb, kv_block=kb, n_forced_tail=2 * kb)
+    assert lib.abatt_plan_rows(ctypes.byref(p.c())) == p.R
+    assert p.n_kbs == 2048 // kb and p.n_kb == p.n_kbs + 2
+    assert ab.max_nnz(p) == p.R * p.n_kb
 
 
 def test_argument_checks_before_any_hip_call(lib):
