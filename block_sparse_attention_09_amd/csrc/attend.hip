@@ -14,17 +14,20 @@
 //     B operand of S^T = K Q^T (bf16 MFMA 32x32x16, fp32 accumulation), so a
 //     lane ends up holding 32 logits of ONE query (lane%32) and the row max
 //     needs a single exchange between the two half-waves;
-//   * keys arrive in chunks of 16 kept blocks = 64 keys.  Each 4-token block
-//     of a head is 4*D*2 contiguous bytes, so one wave-wide 16-byte load
-//     gathers a whole block (D=128) into the K tile.  The block ids of a
-//     chunk are fetched once per wave and broadcast with readlane.  V is
-//     converted to fp16 while it is staged (exact for bf16 values in fp16's
-//     normal range) and stored row-major; the PV operand is read with the
-//     gfx950 LDS transpose read, so PV runs as O^T = V^T P^T on fp16 MFMA with
-//     the probabilities straight from the softmax registers: the key order
-//     inside an MFMA k-step is chosen to match what each lane already holds;
-//   * two LDS buffers, global loads for chunk c+1 issued before chunk c is
-//     computed, one barrier per chunk;
+//   * keys arrive in chunks of 64 = 16 groups of 4 consecutive keys of the
+//     row's key sequence (one kept 4-token block per group; longer blocks
+//     span several groups).  A group of a head is 4*D*2 contiguous bytes, so
+//     one wave-wide 16-byte load moves a whole group (D=128).  The block ids
+//     of a chunk are fetched once per wave and broadcast with readlane.  K
+//     goes straight to LDS by direct buffer loads (gathered rows) into a tile
+//     with an XOR slot swizzle; V is loaded into registers and converted to
+//     fp16 while it is staged (exact for bf16 values in fp16's normal range),
+//     then stored row-major; the PV operand is read with the gfx950 LDS
+//     transpose read, so PV runs as O^T = V^T P^T on fp16 MFMA with the
+//     probabilities straight from the softmax registers: the key order inside
+//     an MFMA k-step is chosen to match what each lane already holds;
+//   * two LDS stages: K and V of chunk c+1 arrive while chunk c is computed,
+//     one barrier per chunk;
 //   * online softmax in the exp2 domain; the running max is only moved when
 //     a chunk raises it by more than 8 (log2 units), so most chunks skip the
 //     rescale of the accumulators (p then stays below 2^8, fine for fp16);
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     issue_loads(min(c + 2, clast));   // V of chunk c+2 -> registers
     fetch_ids(min(c + 3, clast), id_far, lw_far);
 
-    // S^T tile: lane holds query l32, keys 32*tt + 8*g + 4*hh + (0..3) = block 8tt+2g+hh
+    // S^T tile: lane holds query l32, keys 32*tt + 8*g + 4*hh + (0..3) = group 8tt+2g+hh
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {

@@ -110,8 +110,8 @@ size_t abatt_sampler_workspace_bytes(const abatt_problem_t *p);
  * abatt_plan -- IBCS selector followed by SIP sampling.
  *
  * [hamidun] "AB-Attention's three techniques", IBCS and SIP paragraphs, and
- * the third technique (4-token key blocks):
- *   1. mean key of every 4-token key block;
+ * the third technique (4-token key blocks; kv_block may select another size):
+ *   1. mean key of every sparse key block (kv_block consecutive tokens);
  *   2. per 128-query block, Lloyd k-means with n_clusters centroids (init at
  *      the evenly spaced members, kmeans_iters iterations); weight of a
  *      cluster = share of the block's queries in it;
@@ -141,8 +141,9 @@ abatt_status abatt_plan(const abatt_problem_t *p, const void *Q, const void *K,
  *
  * [hamidun] three techniques, SIP: ordinary softmax attention whose logits
  * get the shift log(1/pi) of their block (Horvitz-Thompson weighting), and
- * third technique / [zerohour] key facts: the kept 4-token K/V blocks are
- * gathered by index into full compute tiles, tokens are not permuted.
+ * third technique / [zerohour] key facts: the kept 4-token K/V blocks
+ * (kv_block tokens in general) are gathered by index into full compute
+ * tiles, tokens are not permuted.
  * For query i of row r and kept token t of block j(t):
  *   z_t = scale * q_i . k_t + logw_j(t);  o_i = sum_t e^(z_t - M) v_t / l,
  *   l = sum_t e^(z_t - M);  lse_i = M + ln l  (natural log).
@@ -169,7 +170,8 @@ abatt_status abatt_dense(const abatt_problem_t *p, const void *Q, const void *K,
  * Test hooks: the selector's kernels entered part-way.
  *
  * abatt_key_means: kmean [B,H,n_kbs,D] fp32 device = mean of each sparse
- * 4-token key block ([hamidun] three techniques, IBCS: averaged keys).
+ * key block of kv_block tokens ([hamidun] three techniques, IBCS: averaged
+ * keys).
  *
  * abatt_scores: steps 1-3 of abatt_plan.  S [R, n_kbs] fp32 device;
  * centroids [R, n_clusters, D] fp32 device and weights [R, n_clusters] fp32
