@@ -1,0 +1,108 @@
+"""Attention numerics away from the benchmark's gentle inputs.
+
+The plan is built by the caller (random kept blocks, ascending per row) and
+given to both sides, so these tests isolate the attention kernels:
+  * sharp logits (q and k scaled so that scale * q.k has a spread of tens of
+    nats): the running max moves often and the accumulators are rescaled;
+  * a row max that rises chunk after chunk (every chunk forces a rescale);
+  * large log-weight shifts (pi down to ~1e-13, logw up to 30);
+  * large values (|v| ~ 1e3): the bar scales with the values, max-abs
+    1e-2 * 1e3 (outputs are averages of values that partly cancel, while the
+    fp16 probabilities' rounding error scales with |v|, not with |o|);
+  * logits that all tie (uniform attention).
+Bar as everywhere: the oracle's float64 result rounded like the output, bf16
+max-abs 1e-2 (or one bf16 step) and mean-rel 1e-3, fp32 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import LSE_TOL, TOL, check_output, errors, round_ref, say, to_dev
+from workloads import round_like
+
+pytestmark = pytest.mark.gpu
+
+ab = pytest.importorskip("block_sparse_attention_09_amd")
+
+
+def _plan(rng, op, frac, logw_hi):
+    rows, ci, lw = [0], [], []
+    for _ in range(op.R):
+        keep = np.sort(rng.choice(op.n_kb, max(1, int(frac * op.n_kb)), replace=False))
+        ci.append(keep.astype(np.int32))
+        lw.append(rng.uniform(0.0, logw_hi, len(keep)).astype(np.float32))
+        rows.append(rows[-1] + len(keep))
+    return np.array(rows, dtype=np.int64), np.concatenate(ci), np.concatenate(lw)
+
+
+def _run(name, q, k, v, dtype, frac=0.3, logw_hi=3.0, seed=0, v_scale=1.0):
+    B, H, N, D = q.shape
+    op = oracle.Problem(B=B, H=H, N=N, D=D)
+    rng = np.random.default_rng(seed)
+    rp, ci, lw = _plan(rng, op, frac, logw_hi)
+    O, L = oracle.attend(q, k, v, oracle.Plan(rp, ci, lw), op)
+    prob = ab.Problem(B, H, N, D, dtype=dtype)
+    pl = ab.make_plan(rp, ci, lw, "cuda")
+    o, lse = ab.attend(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), pl, problem=prob,
+                       return_lse=True)
+    torch.cuda.synchronize()
+    say(f"{name} {dtype}: |logit| spread up to {np.abs(L).max():.1f}")
+    if v_scale == 1.0:
+        check_output(o, O, dtype, f"{name} {dtype}")
+    else:
+        mx, mr = errors(o.float().cpu().numpy().astype(np.float64), round_ref(O, dtype))
+        say(f"{name} {dtype}: max-abs {mx:.3e} (bar {TOL[dtype][0] * v_scale:.1e}) mean-rel {mr:.3e}")
+        assert mx <= TOL[dtype][0] * v_scale and mr <= TOL[dtype][1]
+    lh = lse.cpu().numpy()
+    # log-sum-exp: absolute bar relative to the size of the logits involved
+    assert np.abs(lh - L).max() <= LSE_TOL[dtype] * max(1.0, np.abs(L).max() / 8)
+
+
+def _qkv(seed, N, D, dtype, qk_scale=1.0, v_scale=1.0):
+    rng = np.random.default_rng(seed)
+    q = (qk_scale * rng.standard_normal((1, 2, N, D))).astype(np.float32)
+    k = (qk_scale * rng.standard_normal((1, 2, N, D))).astype(np.float32)
+    v = (v_scale * rng.standard_normal((1, 2, N, D))).astype(np.float32)
+    return tuple(round_like(x, dtype) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_sharp_logits(dtype, D):
+    # scale * q.k has a standard deviation of qk_scale^2 = 25 nats
+    q, k, v = _qkv(1, 2048, D, dtype, qk_scale=5.0)
+    _run("sharp", q, k, v, dtype)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_rising_max_rescales_every_chunk(dtype, D):
+    N = 4096
+    q, k, v = _qkv(2, N, D, dtype)
+    # keys grow along one direction the queries share: logits rise with the key index
+    ramp = np.linspace(0.0, 40.0, N, dtype=np.float32)[None, None, :, None]
+    d = np.zeros((1, 1, 1, D), dtype=np.float32)
+    d[..., 0] = 1.0
+    q = round_like(q + 2.0 * d, dtype)
+    k = round_like(k + ramp * d * np.sqrt(D) / 2.0, dtype)
+    _run("rising max", q, k, v, dtype, frac=0.5)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_large_shifts(dtype, D):
+    q, k, v = _qkv(3, 2048, D, dtype)
+    _run("large logw", q, k, v, dtype, frac=0.1, logw_hi=30.0)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_large_values(dtype, D):
+    q, k, v = _qkv(4, 2048, D, dtype, v_scale=1000.0)
+    _run("large v", q, k, v, dtype, v_scale=1000.0)
+
+
+def test_uniform_attention():
+    N, D = 1024, 128
+    q = np.zeros((1, 2, N, D), dtype=np.float32)
+    k = np.zeros_like(q)
+    v = round_like(np.random.default_rng(5).standard_normal((1, 2, N, D)).astype(np.float32),
+                   "bf16")
+    _run("uniform", q, k, v, "bf16", logw_hi=0.0)
