@@ -101,8 +101,12 @@ __global__ __launch_bounds__(256) void k_kmeans(const T* __restrict__ Q, float* 
         a = c;
       }
     }
+    // an assignment equal to the previous one is a fixed point: the update
+    // would reproduce the centroids and counts, and so would every later
+    // iteration, so the loop ends with the same result it would reach at iters
+    const bool changed = h == 0 && valid && (it == 0 || assign[p] != a);
     if (h == 0 && valid) assign[p] = a;
-    __syncthreads();
+    if (!__syncthreads_or(changed)) break;
     // member lists in ascending token order (wave 0)
     if (t < 64) {
       const int a0 = assign[t], a1 = assign[t + 64];
@@ -265,8 +269,10 @@ __global__ __launch_bounds__(256) void k_kmeans_mfma(const uint16_t* __restrict_
   __syncthreads();
 
   int cnt = 0;
+  int prev[2] = {-1, -1};  // this lane's points' assignments in the last iteration
   for (int it = 0; it < iters; ++it) {
     // assignment: nearest centroid by |mu_c|^2 - 2 x.mu_c; ties -> lower index
+    bool changed = false;
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -304,12 +310,17 @@ __global__ __launch_bounds__(256) void k_kmeans_mfma(const uint16_t* __restrict_
       if constexpr (C > 8) pick(pair_x32(best), pair_x32(__int_as_float(a)));
       // one-hot column of point p (rows c >= C and points p >= n stay zero)
       const int p = 32 * w + 16 * u + i;
+      changed |= p < n && a != prev[u];
+      prev[u] = a;
       if (4 * g < C && p < n) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) oh[(4 * g + v) * OS + p] = a == 4 * g + v ? 0x3f80u : 0u;
       }
     }
-    __syncthreads();
+    // an assignment equal to the previous one is a fixed point: the update
+    // would reproduce the centroids and counts (and so would every later
+    // iteration), so the loop ends with the result it would reach at iters
+    if (!__syncthreads_or(changed)) break;
     // update: member sums on the matrix cores; counts from the one-hot bits
     f32x4 sum[UT];
 #pragma unroll
