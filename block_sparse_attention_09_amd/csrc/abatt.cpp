@@ -57,12 +57,14 @@ abatt_status make_shape(const abatt_problem_t* p, Shape* s) {
   return ABATT_OK;
 }
 
-// Dense attention accepts any N (keys past N are masked); the other checks
-// are the same as for the plan problem.
+// Dense attention accepts any N (keys past N are masked) and ignores the
+// key-block size and the forced tail (it runs over every key in groups of 4);
+// the other checks are the same as for the plan problem.
 abatt_status make_dense_shape(const abatt_problem_t* p, Shape* s) {
   if (p == nullptr) return ABATT_EINVAL;
   abatt_problem_t q = *p;
   q.n_forced_tail = 0;
+  q.kv_block = 4;
   const int N = q.N;
   if (N > 0 && N % 4 != 0) q.N = N + (4 - N % 4);  // only for the block checks
   abatt_status st = make_shape(&q, s);

@@ -113,3 +113,15 @@ def test_budget_one_is_dense_block_sizes(kb):
     torch.cuda.synchronize()
     assert pl.nnz() == op.R * op.n_kb
     check_output(o, Od, "bf16", f"budget 1, kb={kb}")
+
+
+def test_dense_ignores_block_size():
+    # dense attention runs over every key: the problem's key-block size (here
+    # one that does not divide N) changes nothing
+    rng = np.random.default_rng(7)
+    q, k, v = (torch.from_numpy(rng.standard_normal((1, 2, 1000, 128)).astype(np.float32))
+               .to(torch.bfloat16).cuda() for _ in range(3))
+    ref = ab.dense(q, k, v, problem=ab.Problem(1, 2, 1000, 128))
+    got = ab.dense(q, k, v, problem=ab.Problem(1, 2, 1000, 128, kv_block=128))
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
