@@ -22,7 +22,11 @@
 //     goes straight to LDS by direct buffer loads (gathered rows) into a tile
 //     with an XOR slot swizzle; V is loaded into registers and converted to
 //     fp16 while it is staged (exact for bf16 values in fp16's normal range),
-//     then stored row-major; the PV operand is read with the gfx950 LDS
+//     then stored row-major.  K and V of a group come from one row
+//     computation, and at D=128 the group's row base is wave-uniform and
+//     rides in the loads' scalar offset, so the gather costs few vector
+//     instructions (the kernel's issue slots are its limit: an MFMA holds
+//     the vector issue for about half its duration); the PV operand is read with the gfx950 LDS
 //     transpose read, so PV runs as O^T = V^T P^T on fp16 MFMA with the
 //     probabilities straight from the softmax registers: the key order inside
 //     an MFMA k-step is chosen to match what each lane already holds;
@@ -78,15 +82,16 @@ __device__ __forceinline__ void dma_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// 16 bytes per lane from a buffer straight into LDS, lane l's bytes at
-// lds_addr + 16 l.  Written as inline asm so that the compiler does not track
-// it: its own wait insertion would otherwise make every later LDS read wait
-// for it.  The caller waits (dma_barrier) before the stage is read.
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, int voff,
+// 16 bytes per lane from byte soff + voff of a buffer straight into LDS, lane
+// l's bytes at lds_addr + 16 l (the range check covers voff, not the
+// wave-uniform soff).  Written as inline asm so that the compiler does not
+// track it: its own wait insertion would otherwise make every later LDS read
+// wait for it.  The caller waits (dma_barrier) before the stage is read.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, int voff, int soff,
                                                   uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "v"(voff), "s"(rs), "s"(lds_addr)
+               : "v"(voff), "s"(rs), "s"(soff), "s"(lds_addr)
                : "memory", "m0");
 }
 
@@ -108,10 +113,9 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   constexpr int DT = D / 32;          // PV output tiles
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int SLOTS = 2 * D / 64;   // 16-byte loads per lane per chunk, for K and for V
-  constexpr int BPS = 64 / (4 * CPR); // 4-key groups covered by one slot of a wave (1 or 2)
+  constexpr int BPS = 64 / (4 * CPR); // 4-key groups covered by one wave-wide load (1 or 2)
   constexpr int GROUP_BYTES = 4 * D * 2;  // one group of 4 keys
-  constexpr int LPB = GROUP_BYTES / 16;   // lanes of one direct K load per group (64 or 32)
-  constexpr int BPI = 64 / LPB;           // groups per direct K load (1 or 2)
+  static_assert(SLOTS * BPS == 4, "a wave moves 4 groups of each chunk");
   // K tile: row-major, 16-byte slot s of row r stored at s ^ (r % CPR)
   // (conflict-free operand reads without padding; the direct loads place each
   // lane's 16 bytes at a fixed LDS position, so the swizzle is chosen through
@@ -164,85 +168,89 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   // shift of group j & 15 (repeated for blocks longer than 4), branch-free.
   auto group_block = [&](int c, int g) { return (64 * c + 4 * g) >> lkb; };
   auto group_token = [&](int c, int g) { return (64 * c + 4 * g) & kbmask; };
+  // The row's ids and shifts are read through bounds-checked buffers: entries
+  // past the row read zero, and valid_id rejects them by position.
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(col_idx + start), (short)0, nblk * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(logw + start), (short)0, nblk * 4, 0x00020000);
   auto fetch_ids = [&](int c, int& id, float& lw) {
-    const int idx = group_block(c, lane & 15);
-    if constexpr (kGather) {
-      const int64_t at = start + (idx < nblk ? idx : nblk - 1);
-      id = col_idx[at];
-      lw = logw[at];
-    } else {
-      id = idx;
-      lw = 0.f;
-    }
+    const int idx = group_block(c, lane & 15) * 4;
+    id = (int)__builtin_amdgcn_raw_buffer_load_b32(crs, idx, 0, 0);
+    lw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lrs, idx, 0, 0));
   };
-  // validity is applied when the ids are used (keeps the loads in flight)
+  // validity is applied when the ids are first used (keeps the loads in flight)
   auto valid_id = [&](int c, int raw) -> bool {
-    if constexpr (kGather) return group_block(c, lane & 15) < nblk && raw >= 0 && raw < n_kb;
-    return true;
+    return group_block(c, lane & 15) < nblk && raw >= 0 && raw < n_kb;
   };
 
-  // lane -> (group within the slot, key within the group, 16-byte chunk)
+  // lane -> (group within a load, key within the group, 16-byte chunk); one
+  // wave-wide 16-byte load covers BPS groups of 4 rows
   const int sub = lane / (4 * CPR);
   const int key = (lane % (4 * CPR)) / CPR;
   const int dc = lane % CPR;
-  const int lane_off = (key * D + 8 * dc) * 2;
   constexpr int ROW_BYTES = D * 2;
+  // the lane's part of a group's offset: its row in the group and its 16-byte
+  // chunk, plain for V, slot-swizzled for the K tile (group g holds tile rows
+  // 4g..4g+3)
+  const int vlane = key * ROW_BYTES + (dc << 4);
+  auto klane = [&](int g) { return key * ROW_BYTES + ((dc ^ ((4 * g + key) % CPR)) << 4); };
 
-  // K goes straight to LDS for gathered rows; dense rows stage it through
-  // registers like V (measured faster there)
+  // Gathered rows: K goes straight to LDS, V through registers (converted to
+  // fp16 on its way to LDS).  Dense rows stage K through registers too
+  // (measured faster there).
   u32x4 vpre[SLOTS], kpre[kGather ? 1 : SLOTS];
-  int id_next = 0, id_far = 0;       // raw ids of chunks c+1 and c+2
-  float lw_next = 0.f, lw_far = 0.f;
-  float lw_store = 0.f;
+  int id_next = 0;                   // raw ids of the next chunk to start (gathered rows)
+  float lw_next = 0.f;
 
-  // The whole row offset goes in the per-lane offset, which the buffer range
-  // check covers: rows past N (the dense path's last partial group) read zero.
-  auto issue_loads = [&](int c) {    // V (dense: K and V) of chunk c, from id_next
+  // Gathered rows: K of chunk c into K stage `stage` (one direct load per
+  // 1 KB) and V of chunk c into registers, both from one row computation per
+  // group.  The ids `idv` are validated, so every row lies inside the head:
+  // when a load covers one group (D = 128) the group's row base is
+  // wave-uniform and goes in the scalar offset.
+  auto issue_kv = [&](int c, int idv, int stage) {
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) {
+      const int b0 = 4 * wv + BPS * j;
+      const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(
+          &Ks[stage][b0 * (GROUP_BYTES / 2)]);
+      if constexpr (BPS == 1) {
+        const int soff = __builtin_amdgcn_readfirstlane(
+            ((__builtin_amdgcn_readlane(idv, b0) << lkb) + group_token(c, b0)) * ROW_BYTES);
+        buffer_load_lds16(krs, klane(b0), soff, lds);
+        vpre[j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vlane, soff, 0));
+      } else {
+        const int r0 = (__builtin_amdgcn_readlane(idv, b0) << lkb) + group_token(c, b0);
+        const int r1 = (__builtin_amdgcn_readlane(idv, b0 + 1) << lkb) + group_token(c, b0 + 1);
+        const int rowoff = (sub ? r1 : r0) * ROW_BYTES;
+        buffer_load_lds16(krs, rowoff + klane(b0 + sub), 0, lds);
+        vpre[j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, rowoff + vlane, 0, 0));
+      }
+    }
+  };
+  // Gathered rows: validate the ids of chunk c (in id_next) once, record its
+  // shifts in stage `stage` and issue its K and V.
+  auto start_chunk = [&](int c, int stage) {
     const bool ok = valid_id(c, id_next);
-    const int idv = ok ? id_next : 0;
-    lw_store = ok ? lw_next * kLog2e : -INFINITY;
+    if (t < 16) lwb[stage][t] = ok ? lw_next * kLog2e : -INFINITY;
+    issue_kv(c, ok ? id_next : 0, stage);
+  };
+  // Dense rows: K and V of chunk c (keys 64c..64c+63) into registers.  The
+  // whole row offset goes in the per-lane offset, which the buffer range
+  // check covers: rows past N (the last partial group) read zero.
+  auto issue_dense = [&](int c) {
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
-      const int g0 = 4 * wv + i * BPS;
-      int row0;                       // first row of this lane's group
-      if constexpr (BPS == 1) {
-        row0 = (__builtin_amdgcn_readlane(idv, g0) << lkb) + group_token(c, g0);
-      } else {
-        const int r0 = (__builtin_amdgcn_readlane(idv, g0) << lkb) + group_token(c, g0);
-        const int r1 = (__builtin_amdgcn_readlane(idv, g0 + 1) << lkb) + group_token(c, g0 + 1);
-        row0 = sub ? r1 : r0;
-      }
-      const int voff = row0 * ROW_BYTES + lane_off;
-      if constexpr (!kGather)
-        kpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff, 0, 0));
+      const int voff = (64 * c + 4 * (4 * wv + i * BPS + sub)) * ROW_BYTES + vlane;
+      kpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff, 0, 0));
       vpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, 0, 0));
     }
   };
-  // K of chunk c (ids `raw`) straight into K stage buf: wave wv moves groups
-  // 4wv..4wv+3, one direct load per 1 KB.  The row offset is in the per-lane
-  // offset, which the buffer range check covers.
-  auto issue_k = [&](int c, int raw, int stage) {
-    if constexpr (!kGather) return;
-    uint16_t* kst = Ks[stage];
-    const int idv = valid_id(c, raw) ? raw : 0;
-#pragma unroll
-    for (int j = 0; j < 4 / BPI; ++j) {
-      const int b0 = 4 * wv + BPI * j;
-      int row0 = (__builtin_amdgcn_readlane(idv, b0) << lkb) + group_token(c, b0);
-      if constexpr (BPI == 2) {
-        const int r1 = (__builtin_amdgcn_readlane(idv, b0 + 1) << lkb) + group_token(c, b0 + 1);
-        row0 = lane >= LPB ? r1 : row0;
-      }
-      const int b = b0 + lane / LPB;
-      const int rib = (lane % LPB) / CPR;
-      const int trow = 4 * b + rib;
-      const int voff = (row0 + rib) * ROW_BYTES + (((lane % CPR) ^ (trow % CPR)) << 4);
-      buffer_load_lds16(krs, voff,
-                        (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(
-                            &kst[b0 * (GROUP_BYTES / 2)]));
-    }
-  };
-  auto store_chunk = [&](int buf) {  // V of the chunk in registers, with its shifts
+  // The chunk in registers into stage buf: V converted to fp16 (exact for
+  // bf16 values in fp16's normal range); dense rows: K as well.
+  auto store_regs = [&](int buf) {
     uint16_t* vst = Vs[buf];
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
@@ -256,7 +264,6 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
                              __uint_as_float(vpre[i][e] & 0xffff0000u));
       *reinterpret_cast<u32x4*>(&vst[row * D + 8 * (dc ^ vswz<D>(row))]) = hv;
     }
-    if (t < 16) lwb[buf][t] = lw_store;
   };
 
   f32x16 oacc[DT];
@@ -266,25 +273,28 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   float lsum0 = 0.f, lsum1 = 0.f;
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  // Pipeline: chunk c is computed from LDS stage c%2.  At the top of
-  // iteration c the free stage (c+1)%2 receives K of chunk c+1 by direct
-  // loads (dense rows: from registers) and V of chunk c+1 from the registers
-  // (loaded during iteration c-1), then V of chunk c+2 is requested into the
-  // registers and the block ids of chunk c+3 are fetched.  The barrier that ends iteration c waits for all
-  // of it, so every load has a whole iteration to land.  Chunk indices are
-  // clamped to the last chunk so the prefetch code runs unconditionally; the
-  // cost is a few redundant loads at the end.
+  // Pipeline: chunk c is computed from LDS stage c%2; the other stage is free
+  // during iteration c.  Gathered rows: at the top of iteration c the ids of
+  // chunk c+1 (fetched during iteration c-1) are validated, K of chunk c+1
+  // goes to the free stage by direct loads and V of chunk c+1 to registers,
+  // and the ids of chunk c+2 are requested; after the chunk's PV the V
+  // registers are converted into the free stage.  Dense rows: chunk c+1 goes
+  // from the registers to the free stage and chunk c+2 is requested into the
+  // registers.  The barrier that ends iteration c waits for all of it, so
+  // every load has a whole iteration to land.  Chunk indices are clamped to
+  // the last chunk so the prefetch code runs unconditionally; the cost is a
+  // few redundant loads at the end.
   const int clast = nchunk > 0 ? nchunk - 1 : 0;
   if (nchunk > 0) {
-    fetch_ids(0, id_next, lw_next);
-    issue_k(0, id_next, 0);
-    issue_loads(0);
-    fetch_ids(min(1, clast), id_far, lw_far);
-    store_chunk(0);
-    id_next = id_far;
-    lw_next = lw_far;
-    issue_loads(min(1, clast));
-    fetch_ids(min(2, clast), id_far, lw_far);
+    if constexpr (kGather) {
+      fetch_ids(0, id_next, lw_next);
+      start_chunk(0, 0);
+      fetch_ids(min(1, clast), id_next, lw_next);
+    } else {
+      issue_dense(0);
+    }
+    store_regs(0);
+    if constexpr (!kGather) issue_dense(min(1, clast));
   }
   dma_barrier();
 
@@ -295,13 +305,13 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   auto step = [&](int c, int buf) {
     const uint16_t* kst = Ks[buf];
     const uint16_t* vst = Vs[buf];
-    // id_next holds the ids of chunk c+1 here
-    issue_k(min(c + 1, clast), id_next, buf ^ 1);  // K of chunk c+1 -> free stage
-    store_chunk(buf ^ 1);    // V of chunk c+1 (registers) -> free stage
-    id_next = id_far;
-    lw_next = lw_far;
-    issue_loads(min(c + 2, clast));   // V of chunk c+2 -> registers
-    fetch_ids(min(c + 3, clast), id_far, lw_far);
+    if constexpr (kGather) {
+      start_chunk(min(c + 1, clast), buf ^ 1);          // K, V of chunk c+1
+      fetch_ids(min(c + 2, clast), id_next, lw_next);   // ids of chunk c+2
+    } else {
+      store_regs(buf ^ 1);                // chunk c+1: registers -> free stage
+      issue_dense(min(c + 2, clast));     // chunk c+2 -> registers
+    }
 
     // S^T tile: lane holds query l32, keys 32*tt + 8*g + 4*hh + (0..3) = group 8tt+2g+hh
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
@@ -339,7 +349,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        lwg[4 * tt + g] = lwb[buf][8 * tt + 2 * g + hh];
+        lwg[4 * tt + g] = kGather ? lwb[buf][8 * tt + 2 * g + hh] : 0.f;
         const float gm = fmaxf(fmaxf(sacc[tt][4 * g], sacc[tt][4 * g + 1]),
                                fmaxf(sacc[tt][4 * g + 2], sacc[tt][4 * g + 3]));
         mloc = fmaxf(mloc, fmaf(gm, scale_log2, lwg[4 * tt + g]));
@@ -397,6 +407,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
         }
       }
     }
+    if constexpr (kGather) store_regs(buf ^ 1);   // V of chunk c+1 -> free stage
     dma_barrier();
   };
   if constexpr (kGather) {
