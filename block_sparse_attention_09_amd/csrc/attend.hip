@@ -25,8 +25,8 @@
 //     then stored row-major.  K and V of a group come from one row
 //     computation, and at D=128 the group's row base is wave-uniform and
 //     rides in the loads' scalar offset, so the gather costs few vector
-//     instructions (the kernel's issue slots are its limit: an MFMA holds
-//     the vector issue for about half its duration); the PV operand is read with the gfx950 LDS
+//     instructions (vector issue is the kernel's limit: an MFMA holds it for
+//     about half its duration).  The PV operand is read with the gfx950 LDS
 //     transpose read, so PV runs as O^T = V^T P^T on fp16 MFMA with the
 //     probabilities straight from the softmax registers: the key order inside
 //     an MFMA k-step is chosen to match what each lane already holds;
@@ -407,16 +407,19 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
         }
       }
     }
-    // keep four transpose reads (two MFMAs' operands) in flight ahead of the
-    // PV MFMAs (measured: 1% faster than the compiler's own order; two, six or
-    // eight ahead are slower)
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    // gathered rows: keep four transpose reads (two MFMAs' operands) in flight
+    // ahead of the PV MFMAs (measured: 1% faster than the compiler's own
+    // order; two, six or eight ahead are slower, and so is the dense kernel
+    // with it)
+    if constexpr (kGather) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * 2 * DT - 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int i = 0; i < 2 * 2 * DT - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     if constexpr (kGather) store_regs(buf ^ 1);   // V of chunk c+1 -> free stage
     dma_barrier();
   };
