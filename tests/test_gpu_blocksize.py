@@ -100,9 +100,11 @@ def test_plan_and_attend_block_sizes(name):
     assert np.abs(lse_h[fin] - L[fin]).max(initial=0.0) <= LSE_TOL[wl.dtype]
 
 
-@pytest.mark.parametrize("kb", [16, 128])
-def test_budget_one_is_dense_block_sizes(kb):
-    wl = Workload("one", B=1, H=1, D=128, grid=(2, 16, 32), kv_block=kb)
+@pytest.mark.parametrize("kb,D", [(16, 128), (128, 128), (4, 64), (64, 64)])
+def test_budget_one_is_dense_block_sizes(kb, D):
+    # every key block of the head, the last rows included, through both gather
+    # forms (one 4-key group per wave-wide load at D = 128, two at D = 64)
+    wl = Workload("one", B=1, H=1, D=D, grid=(2, 16, 32), kv_block=kb)
     q, k, v = make_qkv(wl)
     op = oracle_problem(wl)
     Od, _ = oracle.dense(q, k, v, op)
@@ -112,7 +114,7 @@ def test_budget_one_is_dense_block_sizes(kb):
     o = ab.attend(dq, dk, dv, pl, problem=prob)
     torch.cuda.synchronize()
     assert pl.nnz() == op.R * op.n_kb
-    check_output(o, Od, "bf16", f"budget 1, kb={kb}")
+    check_output(o, Od, "bf16", f"budget 1, kb={kb}, D={D}")
 
 
 def test_dense_ignores_block_size():
