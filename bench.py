@@ -1,16 +1,17 @@
 """Benchmark of the AB-Attention hot path on one MI355X.
 
-One step = abatt_plan (IBCS selector + SIP sampler) followed by abatt_attend
-(gathered sparse attention) over one synthetic layer, inputs already resident
-in HBM.  Default workload: the Wan2.1-14B 720p layer shape (B=1, 40 heads,
+One step = abatt_plan (IBCS selector + SIP sampler), then, for bf16 layers,
+abatt_v_to_f16 (V to fp16 once per call) and abatt_attend_v16 (gathered
+sparse attention, bit-identical to abatt_attend), over one synthetic layer,
+inputs already resident in HBM.  Default workload: the Wan2.1-14B 720p layer shape (B=1, 40 heads,
 75600 tokens = 21x45x80 latent grid, D=128, bf16) at a 10% block budget.
 
 Printed: one JSON line with the step throughput as dense-equivalent TFLOP/s
-(4*B*H*N^2*D per step / step time), the per-call times of attend, plan,
-attend + plan/4 (one plan every four denoising steps) and the library's own
-dense kernel, the roofline of the attention kernel (HIP events around each
-abatt_attend launch on the stream it runs on), and the CPU oracle timed on a
-bounded sample of the same workload.
+(4*B*H*N^2*D per step / step time), the per-call times of attend, the V
+conversion, plan, attend + conversion + plan/4 (one plan every four denoising
+steps) and the library's own dense kernel, the roofline of the attention
+kernel (HIP events around each attention launch on the stream it runs on), and
+the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload wan14b_720p] [--budget 0.10]
     python bench.py --probe copy     # plain device copy, for counter calibration
@@ -168,12 +169,19 @@ def main():
     pl = ab.empty_plan(prob, ab.nnz_bound(prob, budget), q.device)
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
+    # bf16 problems: V converted to fp16 once per call (abatt_v_to_f16), then the
+    # attention's fp16-V form (abatt_attend_v16, bit-identical to abatt_attend)
+    v16 = torch.empty(v.shape, dtype=torch.float16, device=v.device) \
+        if wl.dtype == "bf16" else None
+    va = v if v16 is None else v16
 
     def step(i, ev=None):
         ab.plan(q, k, budget, seed=wl.plan_seed + i, problem=prob, ws=ws, out=pl)
+        if v16 is not None:
+            ab.v_to_f16(v, prob, out=v16)
         if ev is not None:
             ev[0].record(stream)
-        ab.attend(q, k, v, pl, problem=prob, out=o)
+        ab.attend(q, k, va, pl, problem=prob, out=o)
         if ev is not None:
             ev[1].record(stream)
 
@@ -207,6 +215,18 @@ def main():
     torch.cuda.synchronize()
     plan_ms = s2.elapsed_time(e2) / args.steps
 
+    # the V conversion alone
+    convert_ms = 0.0
+    if v16 is not None:
+        s4, e4 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s4.record(stream)
+        for _ in range(args.steps):
+            ab.v_to_f16(v, prob, out=v16)
+        e4.record(stream)
+        torch.cuda.synchronize()
+        convert_ms = s4.elapsed_time(e4) / args.steps
+    call_ms = attend_ms + convert_ms       # the attention path per call
+
     # attend from a cold Infinity Cache: a 512 MB overwrite before each rep,
     # outside the event pair; median over the reps
     attend_cold_ms = None
@@ -217,7 +237,7 @@ def main():
             scratch.fill_(i & 0xFF)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            ab.attend(q, k, v, pl, problem=prob, out=o)
+            ab.attend(q, k, va, pl, problem=prob, out=o)
             b.record(stream)
             torch.cuda.synchronize()
             cold.append(a.elapsed_time(b))
@@ -288,7 +308,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "k_attend_bf16<128,gather>" if wl.dtype == "bf16" else "k_attend_f32",
+            "kernel": "k_attend_bf16<128,gather,fp16 V>" if wl.dtype == "bf16" else "k_attend_f32",
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -297,13 +317,14 @@ def main():
         },
         "detail": {
             "attend_ms": attend_ms,
+            "v_to_f16_ms": convert_ms,
             "plan_ms": plan_ms,
-            "attend_plus_plan_over_4_ms": attend_ms + plan_ms / 4,
+            "attend_plus_plan_over_4_ms": call_ms + plan_ms / 4,
             "dense_ms": dense_ms,
-            "attend_dense_equiv_tflops": dense_flop / (attend_ms * 1e-3) / 1e12,
-            "speedup_attend_vs_dense": (dense_ms / attend_ms) if dense_ms else None,
+            "attend_dense_equiv_tflops": dense_flop / (call_ms * 1e-3) / 1e12,
+            "speedup_attend_vs_dense": (dense_ms / call_ms) if dense_ms else None,
             "speedup_step_vs_dense": (dense_ms / step_ms) if dense_ms else None,
-            "speedup_amortized_vs_dense": (dense_ms / (attend_ms + plan_ms / 4)) if dense_ms else None,
+            "speedup_amortized_vs_dense": (dense_ms / (call_ms + plan_ms / 4)) if dense_ms else None,
             "dense_mfma_frac": (dense_flop / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if dense_ms else None,
             "attend_flop_per_launch": attend_flop,
             "attend_ms_cold_median": attend_cold_ms,

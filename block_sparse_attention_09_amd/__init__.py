@@ -29,7 +29,8 @@ ABATT_F32, ABATT_BF16 = 0, 1
 SYMBOLS = (
     "abatt_plan_rows", "abatt_plan_max_nnz", "abatt_plan_nnz_bound",
     "abatt_plan_workspace_bytes", "abatt_sampler_workspace_bytes", "abatt_plan",
-    "abatt_attend", "abatt_dense", "abatt_key_means", "abatt_scores",
+    "abatt_attend", "abatt_v_to_f16", "abatt_attend_v16", "abatt_dense", "abatt_key_means",
+    "abatt_scores",
     "abatt_plan_from_scores", "abatt_status_str", "abatt_version",
 )
 
@@ -71,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "abatt_plan": (st, [P, vp, vp, ctypes.c_double, ctypes.c_uint64, vp, sz,
                             ctypes.POINTER(_Plan), vp]),
         "abatt_attend": (st, [P, vp, vp, vp, ctypes.POINTER(_Plan), vp, vp, vp]),
+        "abatt_v_to_f16": (st, [P, vp, vp, vp]),
+        "abatt_attend_v16": (st, [P, vp, vp, vp, ctypes.POINTER(_Plan), vp, vp, vp]),
         "abatt_dense": (st, [P, vp, vp, vp, vp, vp, vp]),
         "abatt_key_means": (st, [P, vp, vp, vp]),
         "abatt_scores": (st, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
@@ -248,19 +251,47 @@ def plan(q: torch.Tensor, k: torch.Tensor, budget: float, seed: int = 0,
     return out
 
 
+def _v16_check(prob: Problem, v16: torch.Tensor) -> None:
+    if prob.dtype != "bf16":
+        raise ValueError("fp16 V is for bf16 problems")
+    if not v16.is_cuda or not v16.is_contiguous() or v16.dtype != torch.float16 \
+            or tuple(v16.shape) != (prob.B, prob.H, prob.N, prob.D):
+        raise ValueError(f"expected contiguous float16 [{prob.B},{prob.H},{prob.N},{prob.D}]")
+
+
+def v_to_f16(v: torch.Tensor, problem: Optional[Problem] = None,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 V -> fp16 (round toward zero) for attend's fp16-V form (abatt_v_to_f16)."""
+    prob = problem or Problem.like(v)
+    _qkv_check(prob, v)
+    v16 = torch.empty(v.shape, dtype=torch.float16, device=v.device) if out is None else out
+    _v16_check(prob, v16)
+    _check(load_library().abatt_v_to_f16(ctypes.byref(prob.c()), _ptr(v), _ptr(v16), _stream()))
+    return v16
+
+
 def attend(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pl: Plan,
            problem: Optional[Problem] = None, return_lse: bool = False,
            out: Optional[torch.Tensor] = None):
-    """Gathered attention with the log(1/pi) shift (abatt_attend)."""
+    """Gathered attention with the log(1/pi) shift (abatt_attend).
+
+    A float16 `v` (from v_to_f16) selects abatt_attend_v16, with bit-identical results.
+    """
     prob = problem or Problem.like(q)
-    _qkv_check(prob, q, k, v)
+    v16 = v.dtype == torch.float16
+    _qkv_check(prob, q, k)
+    if v16:
+        _v16_check(prob, v)
+    else:
+        _qkv_check(prob, v)
     _plan_check(prob, pl)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32, device=q.device) \
         if return_lse else None
     cp = pl.c()
-    _check(load_library().abatt_attend(ctypes.byref(prob.c()), _ptr(q), _ptr(k), _ptr(v),
-                                       ctypes.byref(cp), _ptr(o), _ptr(lse), _stream()))
+    fn = load_library().abatt_attend_v16 if v16 else load_library().abatt_attend
+    _check(fn(ctypes.byref(prob.c()), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cp), _ptr(o),
+              _ptr(lse), _stream()))
     return (o, lse) if return_lse else o
 
 

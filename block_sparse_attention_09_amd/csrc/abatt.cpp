@@ -227,7 +227,33 @@ abatt_status abatt_attend(const abatt_problem_t* p, const void* Q, const void* K
   st = check_plan(s, plan, false);
   if (st != ABATT_OK) return st;
   return hip_status(abatt::launch_attend(s, Q, K, V, plan->row_ptr, plan->col_idx, plan->logw,
-                                         plan->capacity, plan->status, O, lse, true, stream));
+                                         plan->capacity, plan->status, O, lse, true, false,
+                                         stream));
+}
+
+abatt_status abatt_v_to_f16(const abatt_problem_t* p, const void* V, void* V16,
+                            hipStream_t stream) {
+  Shape s;
+  abatt_status st = make_shape(p, &s);
+  if (st != ABATT_OK) return st;
+  if (!s.bf16) return ABATT_EUNSUPPORTED;
+  if (V == nullptr || V16 == nullptr || V == V16) return ABATT_EINVAL;
+  return hip_status(abatt::launch_v_to_f16(s, V, V16, stream));
+}
+
+abatt_status abatt_attend_v16(const abatt_problem_t* p, const void* Q, const void* K,
+                              const void* V16, const abatt_plan_t* plan, void* O, float* lse,
+                              hipStream_t stream) {
+  Shape s;
+  abatt_status st = make_shape(p, &s);
+  if (st != ABATT_OK) return st;
+  if (!s.bf16) return ABATT_EUNSUPPORTED;
+  if (Q == nullptr || K == nullptr || V16 == nullptr || O == nullptr) return ABATT_EINVAL;
+  st = check_plan(s, plan, false);
+  if (st != ABATT_OK) return st;
+  return hip_status(abatt::launch_attend(s, Q, K, V16, plan->row_ptr, plan->col_idx,
+                                         plan->logw, plan->capacity, plan->status, O, lse, true,
+                                         true, stream));
 }
 
 abatt_status abatt_dense(const abatt_problem_t* p, const void* Q, const void* K, const void* V,
@@ -237,7 +263,7 @@ abatt_status abatt_dense(const abatt_problem_t* p, const void* Q, const void* K,
   if (st != ABATT_OK) return st;
   if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr) return ABATT_EINVAL;
   return hip_status(abatt::launch_attend(s, Q, K, V, nullptr, nullptr, nullptr, 0, nullptr, O,
-                                         lse, false, stream));
+                                         lse, false, false, stream));
 }
 
 const char* abatt_status_str(abatt_status s) {

@@ -102,7 +102,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base
                                            0x00020000);
 }
 
-template <int D, bool kGather>
+// kV16: V arrives already converted to fp16 (gathered rows only) and goes
+// to LDS by direct loads like K.
+template <int D, bool kGather, bool kV16>
 __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
@@ -116,6 +118,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   constexpr int BPS = 64 / (4 * CPR); // 4-key groups covered by one wave-wide load (1 or 2)
   constexpr int GROUP_BYTES = 4 * D * 2;  // one group of 4 keys
   static_assert(SLOTS * BPS == 4, "a wave moves 4 groups of each chunk");
+  static_assert(kGather || !kV16, "fp16 V is a gathered-row form");
   // K tile: row-major, 16-byte slot s of row r stored at s ^ (r % CPR)
   // (conflict-free operand reads without padding; the direct loads place each
   // lane's 16 bytes at a fixed LDS position, so the swizzle is chosen through
@@ -195,11 +198,18 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   // 4g..4g+3)
   const int vlane = key * ROW_BYTES + (dc << 4);
   auto klane = [&](int g) { return key * ROW_BYTES + ((dc ^ ((4 * g + key) % CPR)) << 4); };
+  // fp16 V by direct loads: the lane's source chunk carries the V tile's swizzle
+  // (chunk c of tile row r at c ^ vswz(r)), and group g's 4 rows land at row 4g
+  auto vlane_t = [&](int g) { return key * ROW_BYTES + ((dc ^ vswz<D>(4 * g + key)) << 4); };
+  auto vlds = [&](int stage, int g) {
+    return (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(
+        &Vs[stage][g * (GROUP_BYTES / 2)]);
+  };
 
   // Gathered rows: K goes straight to LDS, V through registers (converted to
   // fp16 on its way to LDS).  Dense rows stage K through registers too
   // (measured faster there).
-  u32x4 vpre[SLOTS], kpre[kGather ? 1 : SLOTS];
+  u32x4 vpre[kV16 ? 1 : SLOTS], kpre[kGather ? 1 : SLOTS];
   int id_next = 0;                   // raw ids of the next chunk to start (gathered rows)
   float lw_next = 0.f;
 
@@ -218,15 +228,21 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
         const int soff = __builtin_amdgcn_readfirstlane(
             ((__builtin_amdgcn_readlane(idv, b0) << lkb) + group_token(c, b0)) * ROW_BYTES);
         buffer_load_lds16(krs, klane(b0), soff, lds);
-        vpre[j] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vlane, soff, 0));
+        if constexpr (kV16)
+          buffer_load_lds16(vrs, vlane_t(b0), soff, vlds(stage, b0));
+        else
+          vpre[j] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vlane, soff, 0));
       } else {
         const int r0 = (__builtin_amdgcn_readlane(idv, b0) << lkb) + group_token(c, b0);
         const int r1 = (__builtin_amdgcn_readlane(idv, b0 + 1) << lkb) + group_token(c, b0 + 1);
         const int rowoff = (sub ? r1 : r0) * ROW_BYTES;
         buffer_load_lds16(krs, rowoff + klane(b0 + sub), 0, lds);
-        vpre[j] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, rowoff + vlane, 0, 0));
+        if constexpr (kV16)
+          buffer_load_lds16(vrs, rowoff + vlane_t(b0 + sub), 0, vlds(stage, b0));
+        else
+          vpre[j] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, rowoff + vlane, 0, 0));
       }
     }
   };
@@ -293,7 +309,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     } else {
       issue_dense(0);
     }
-    store_regs(0);
+    if constexpr (!kV16) store_regs(0);
     if constexpr (!kGather) issue_dense(min(1, clast));
   }
   dma_barrier();
@@ -420,7 +436,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    if constexpr (kGather) store_regs(buf ^ 1);   // V of chunk c+1 -> free stage
+    if constexpr (kGather && !kV16) store_regs(buf ^ 1);   // V of chunk c+1 -> free stage
     dma_barrier();
   };
   if constexpr (kGather) {
@@ -576,7 +592,33 @@ __global__ __launch_bounds__(128) void k_attend_f32(
   }
 }
 
-template <int D, bool kGather>
+// ---------------------------------------------------------------------------
+// bf16 V to fp16 once per call, for the fp16-V form of the gathered kernel:
+// the conversion that kernel otherwise applies while staging V (round toward
+// zero, exact in fp16's normal range), 16 bytes per thread per step.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_v_to_f16(const u32x4* __restrict__ V,
+                                                  u32x4* __restrict__ V16, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) {
+    const u32x4 x = V[i];
+    u32x4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      h[e] = pack_f16_rtz(__uint_as_float(x[e] << 16), __uint_as_float(x[e] & 0xffff0000u));
+    V16[i] = h;
+  }
+}
+
+hipError_t launch_v_to_f16(const Shape& s, const void* V, void* V16, hipStream_t st) {
+  const int64_t n16 = (int64_t)s.B * s.H * s.N * s.D / 8;   // D is a multiple of 8
+  const int64_t blocks = (n16 + 255) / 256;
+  const int grid = (int)(blocks < 16384 ? blocks : 16384);
+  k_v_to_f16<<<grid, 256, 0, st>>>((const u32x4*)V, (u32x4*)V16, n16);
+  return hipGetLastError();
+}
+
+template <int D, bool kGather, bool kV16>
 static void launch_attend_t(const Shape& s, const void* Q, const void* K, const void* V,
                             const int32_t* row_ptr, const int32_t* col_idx, const float* logw,
                             int64_t capacity, const int32_t* status, void* O, float* lse,
@@ -587,7 +629,7 @@ static void launch_attend_t(const Shape& s, const void* Q, const void* K, const 
   if (kGather)
     while ((1 << lkb) < s.kv_block) ++lkb;
   if (s.bf16) {
-    k_attend_bf16<D, kGather><<<s.R, 256, 0, st>>>(
+    k_attend_bf16<D, kGather, kV16><<<s.R, 256, 0, st>>>(
         (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, row_ptr, col_idx, logw,
         capacity, status, (uint16_t*)O, lse, s.N, s.n_qb, s.n_kb, s.R, sl2, lkb);
   } else {
@@ -600,18 +642,23 @@ static void launch_attend_t(const Shape& s, const void* Q, const void* K, const 
 hipError_t launch_attend(const Shape& s, const void* Q, const void* K, const void* V,
                          const int32_t* row_ptr, const int32_t* col_idx, const float* logw,
                          int64_t capacity, const int32_t* status, void* O, float* lse,
-                         bool gather, hipStream_t st) {
+                         bool gather, bool v16, hipStream_t st) {
+#define ABATT_ATTEND(Dv)                                                                     \
+  if (v16)                                                                                   \
+    launch_attend_t<Dv, true, true>(s, Q, K, V, row_ptr, col_idx, logw, capacity, status, O, \
+                                    lse, st);                                                \
+  else if (gather)                                                                           \
+    launch_attend_t<Dv, true, false>(s, Q, K, V, row_ptr, col_idx, logw, capacity, status,   \
+                                     O, lse, st);                                            \
+  else                                                                                       \
+    launch_attend_t<Dv, false, false>(s, Q, K, V, row_ptr, col_idx, logw, capacity, status,  \
+                                      O, lse, st);
   if (s.D == 128) {
-    if (gather)
-      launch_attend_t<128, true>(s, Q, K, V, row_ptr, col_idx, logw, capacity, status, O, lse, st);
-    else
-      launch_attend_t<128, false>(s, Q, K, V, row_ptr, col_idx, logw, capacity, status, O, lse, st);
+    ABATT_ATTEND(128)
   } else {
-    if (gather)
-      launch_attend_t<64, true>(s, Q, K, V, row_ptr, col_idx, logw, capacity, status, O, lse, st);
-    else
-      launch_attend_t<64, false>(s, Q, K, V, row_ptr, col_idx, logw, capacity, status, O, lse, st);
+    ABATT_ATTEND(64)
   }
+#undef ABATT_ATTEND
   return hipGetLastError();
 }
 

@@ -41,10 +41,13 @@ hipError_t launch_sampler(const Shape& s, const float* S, double budget, uint64_
                           void* ws, int32_t* row_ptr, int32_t* col_idx, float* logw,
                           int64_t capacity, int32_t* status, hipStream_t st);
 
-// attend.hip: gathered (plan != null) or dense attention
+// attend.hip: gathered (plan != null) or dense attention; v16: gathered rows
+// with V given as fp16 (bf16 problems)
 hipError_t launch_attend(const Shape& s, const void* Q, const void* K, const void* V,
                          const int32_t* row_ptr, const int32_t* col_idx, const float* logw,
                          int64_t capacity, const int32_t* status, void* O, float* lse,
-                         bool gather, hipStream_t st);
+                         bool gather, bool v16, hipStream_t st);
+// attend.hip: V [B,H,N,D] bf16 -> fp16 (round toward zero)
+hipError_t launch_v_to_f16(const Shape& s, const void* V, void* V16, hipStream_t st);
 
 }  // namespace abatt

@@ -158,6 +158,31 @@ abatt_status abatt_attend(const abatt_problem_t *p, const void *Q, const void *K
                           float *lse, hipStream_t stream);
 
 /*
+ * abatt_v_to_f16, abatt_attend_v16 -- abatt_attend in two steps, for bf16
+ * problems ([hamidun] three techniques: the same gathered attention).
+ *
+ * The bf16 path multiplies the probabilities with V in fp16.  abatt_attend
+ * converts each gathered V block while staging it, once for every plan row
+ * that keeps the block.  abatt_v_to_f16 converts V once per call instead:
+ * V16[i] = V[i] rounded toward zero to fp16, with the same instruction
+ * abatt_attend uses.  That is exact for |v| in fp16's normal range
+ * [2^-14, 65504]; larger magnitudes saturate and smaller ones lose bits.
+ * abatt_attend_v16 then takes V16 in place of V and moves it to LDS by
+ * direct loads, like K.  Its O and lse are bit-identical to abatt_attend's
+ * on the V that V16 came from.
+ *
+ * V, V16: [B,H,N,D] device buffers of 2-byte elements, caller-owned; V16 is
+ * written in full and must not be V.  Other arguments as abatt_attend.
+ * Returns ABATT_EUNSUPPORTED for fp32 problems, and ABATT_EINVAL for NULL
+ * pointers or V16 == V.
+ */
+abatt_status abatt_v_to_f16(const abatt_problem_t *p, const void *V, void *V16,
+                            hipStream_t stream);
+abatt_status abatt_attend_v16(const abatt_problem_t *p, const void *Q, const void *K,
+                              const void *V16, const abatt_plan_t *plan, void *O,
+                              float *lse, hipStream_t stream);
+
+/*
  * abatt_dense -- full softmax attention over every key, no shift: the
  * quadratic baseline the method approximates ([hamidun] introduction;
  * [zerohour] abstract excerpt).  Same layouts, precision and lse convention

@@ -20,7 +20,7 @@ def lib():
 def header_symbols():
     text = open(os.path.join(ROOT, "include", "abatt.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(abatt_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(abatt_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -115,6 +115,14 @@ def test_argument_checks_before_any_hip_call(lib):
     small = ab._Plan(0x1000, 0x1000, 0x1000, 10, 0x1000)
     wsf = lib.abatt_plan_workspace_bytes(P(pf))
     assert lib.abatt_plan(P(pf), fake, fake, 0.1, 0, fake, wsf, P(small), None) == -4
+    # fp16 V: nulls, V16 aliasing V, fp32 problems
+    assert lib.abatt_v_to_f16(P(c), None, fake, None) == -1
+    assert lib.abatt_v_to_f16(P(c), fake, fake, None) == -1
+    assert lib.abatt_attend_v16(P(c), fake, fake, None, P(good), fake, None, None) == -1
+    assert lib.abatt_attend_v16(P(c), fake, fake, fake, P(noarr), fake, None, None) == -1
+    c32 = prob(dtype="f32", D=64).c()
+    assert lib.abatt_v_to_f16(P(c32), fake, ctypes.c_void_p(0x2000), None) == -2
+    assert lib.abatt_attend_v16(P(c32), fake, fake, fake, P(good), fake, None, None) == -2
     # dense accepts N not a multiple of 4 (keys past N are masked) but still checks D
     assert lib.abatt_dense(P(prob(N=1023, D=96).c()), fake, fake, fake, fake, None, None) == -2
 

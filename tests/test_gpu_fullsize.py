@@ -4,7 +4,8 @@ The GPU runs the whole layer (every head, every plan row); the oracle checks a
 sample of rows one by one:
   * plan rows against oracle.plan on the same rows (block agreement >= 99%);
   * attention rows against the oracle run on the GPU's own plan rows (bf16
-    bar: max-abs 1e-2, mean-rel 1e-3 against the oracle rounded to bf16);
+    bar: max-abs 1e-2, mean-rel 1e-3 against the oracle rounded to bf16), and
+    the fp16-V form (V converted once, as bench.py runs it) bit-identical to it;
   * dense rows against the oracle's dense attention of sampled queries.
 Sampled rows lie in the first two heads (the oracle gets those heads' inputs,
 generated on the host by the same seeded recipe).
@@ -108,7 +109,11 @@ def test_fullsize_plan_attend(name):
         assert abs(nnz - expect) < 6 * np.sqrt(op.R * m)
         check_plan_and_attend(f"{name} budget {budget}", wl, budget, wl.plan_seed, q2, k2, v2,
                               q, k, v, prob, op, pl, o)
-        del pl, o
+        # the fp16-V form bench.py times: bit-identical to the attention just checked
+        o16 = ab.attend(q, k, ab.v_to_f16(v, prob), pl, problem=prob)
+        torch.cuda.synchronize()
+        assert torch.equal(o16, o)
+        del pl, o, o16
     if name == "wan14b_720p":
         od = ab.dense(q, k, v, problem=prob)
         torch.cuda.synchronize()
