@@ -1,8 +1,9 @@
 """The library under HIP graph capture and on concurrent streams.
 
 Every entry point only enqueues kernels on the caller's stream (no memsets,
-copies, allocations or synchronisations), so a plan + attend sequence can be
-captured once and replayed, and calls on different streams with their own
+copies, allocations or synchronisations), so a plan + attend sequence (also
+with the V conversion of the fp16-V form) can be captured once and replayed,
+and calls on different streams with their own
 workspaces and plans do not interfere.  Checked bit for bit against eager
 calls: several replays with eager work and synchronisations between them, and
 two streams (default priority) working at once.
@@ -31,8 +32,8 @@ def _eager(prob, q, k, v, budget, seed):
     return pl, o, lse
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
-def test_plan_attend_graph_replays(dtype, D):
+@pytest.mark.parametrize("dtype,D,v16", [("bf16", 128, False), ("bf16", 128, True), ("f32", 64, False)])
+def test_plan_attend_graph_replays(dtype, D, v16):
     wl, (q, k, v) = _inputs(1, dtype, D)
     prob = lib_problem(wl)
     budget, seed = 0.15, 9
@@ -44,19 +45,23 @@ def test_plan_attend_graph_replays(dtype, D):
     ws = ab.workspace(prob, q.device)
     pl = ab.empty_plan(prob, ab.nnz_bound(prob, budget), q.device)
     o = torch.empty_like(q)
+    vh = torch.empty(v.shape, dtype=torch.float16, device=v.device) if v16 else None
+
+    def body(**kw):
+        ab.plan(qs, ks, budget, seed=seed, problem=prob, ws=ws, out=pl)
+        va = ab.v_to_f16(vs, prob, out=vh) if v16 else vs     # fp16-V form: same results
+        return ab.attend(qs, ks, va, pl, problem=prob, out=o, **kw)
 
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):          # warm the binding's code paths off the graph
-        ab.plan(qs, ks, budget, seed=seed, problem=prob, ws=ws, out=pl)
-        ab.attend(qs, ks, vs, pl, problem=prob, out=o)
+        body()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
-        ab.plan(qs, ks, budget, seed=seed, problem=prob, ws=ws, out=pl)
         # the log-sum-exp tensor is allocated inside the capture (graph pool)
-        _, lse_buf = ab.attend(qs, ks, vs, pl, problem=prob, return_lse=True, out=o)
+        _, lse_buf = body(return_lse=True)
 
     other_wl, (q2, k2, v2) = _inputs(2, dtype, D)
     for rep in range(4):
@@ -67,7 +72,7 @@ def test_plan_attend_graph_replays(dtype, D):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        say(f"graph {dtype} replay {rep}: nnz {pl.nnz()}")
+        say(f"graph {dtype}{' v16' if v16 else ''} replay {rep}: nnz {pl.nnz()}")
         assert torch.equal(pl.row_ptr, ref_pl.row_ptr)
         assert torch.equal(pl.col_idx[:n], ref_pl.col_idx[:n])
         assert torch.equal(pl.logw[:n], ref_pl.logw[:n])
