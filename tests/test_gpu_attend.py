@@ -85,8 +85,8 @@ def test_dense_ragged_lengths(N, dtype, D):
     assert np.abs(lse.cpu().numpy() - Ld).max() <= LSE_TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_empty_rows_invalid_ids_and_overflowed_plan(dtype):
+@pytest.mark.parametrize("dtype,v16", [("bf16", False), ("bf16", True), ("f32", False)])
+def test_empty_rows_invalid_ids_and_overflowed_plan(dtype, v16):
     wl = Workload("e", B=1, H=1, D=128 if dtype == "bf16" else 64, grid=(3, 8, 16), dtype=dtype)
     q, k, v = make_qkv(wl)
     op = oracle_problem(wl)
@@ -98,9 +98,11 @@ def test_empty_rows_invalid_ids_and_overflowed_plan(dtype):
     rp = np.cumsum([0] + [len(x) for x in rows])
     ci = np.array(sum(rows, []), np.int32)
     lw = np.array(sum(lws, []), np.float32)
-    say(f"empty/invalid rows {dtype}")
+    say(f"empty/invalid rows {dtype}{' v16' if v16 else ''}")
     gp = ab.make_plan(rp, ci, lw, "cuda")
     dq, dk, dv = (to_dev(x, dtype) for x in (q, k, v))
+    if v16:                        # the fp16-V form takes the same plan
+        dv = ab.v_to_f16(dv, prob)
     o, lse = ab.attend(dq, dk, dv, gp, problem=prob, return_lse=True)
     torch.cuda.synchronize()
     o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
