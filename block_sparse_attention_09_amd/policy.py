@@ -26,7 +26,7 @@ from typing import Dict, Optional, Tuple
 
 import torch
 
-from . import Plan, Problem, attend, dense, plan
+from . import Plan, Problem, attend, dense, plan, v_to_f16
 
 DENSE, BUILD, REUSE = "dense", "build", "reuse"
 
@@ -92,19 +92,24 @@ class ABAttention:
     denoising step s.  Each call runs the library's dense kernel, builds a new
     plan (abatt_plan) and attends with it, or attends with the block's cached
     plan (abatt_attend), as the policy says.  Plans stay on the device between
-    steps; a plan that outgrew its capacity raises.
+    steps; a plan that outgrew its capacity raises.  For bf16 inputs the sparse
+    calls convert V to fp16 once per call and use the attention's fp16-V form
+    (abatt_v_to_f16 + abatt_attend_v16: the same results, a faster kernel)
+    unless ``fp16_v`` is False.
     """
 
     def __init__(self, policy: StepPolicy = StepPolicy(), n_text: int = 0,
-                 n_clusters: int = 8, kmeans_iters: int = 10):
+                 n_clusters: int = 8, kmeans_iters: int = 10, fp16_v: bool = True):
         if n_text % 4:
             raise ValueError("text tokens must fill whole 4-token key blocks")
         self.policy = policy
         self.n_text = n_text
         self.n_clusters = n_clusters
         self.kmeans_iters = kmeans_iters
+        self.fp16_v = fp16_v
         self.step = 0
         self._plans: Dict[int, Tuple[int, Plan, Problem]] = {}
+        self._v16: Optional[torch.Tensor] = None   # reused fp16 copy of V
         self.log: list = []    # (step, block, mode) of every call
 
     def set_step(self, step: int) -> None:
@@ -137,4 +142,8 @@ class ABAttention:
             if not pl.ok():
                 raise RuntimeError("plan outgrew its capacity")
             self._plans[block] = (self.step, pl, prob)
+        if self.fp16_v and v.dtype == torch.bfloat16:
+            if self._v16 is None or self._v16.shape != v.shape or self._v16.device != v.device:
+                self._v16 = torch.empty(v.shape, dtype=torch.float16, device=v.device)
+            v = v_to_f16(v, prob, out=self._v16)
         return attend(q, k, v, self._plans[block][1], problem=prob, return_lse=return_lse)
