@@ -16,6 +16,10 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Device tensors and workspaces are read and written 16 bytes at a time: a
+// pointer that is NULL or not 16-byte aligned is rejected.
+static bool bad(const void* x) { return x == nullptr || (reinterpret_cast<uintptr_t>(x) & 15) != 0; }
+
 // Validates *p; fills *s.  Returns ABATT_OK, ABATT_EINVAL or ABATT_EUNSUPPORTED.
 abatt_status make_shape(const abatt_problem_t* p, Shape* s) {
   if (p == nullptr) return ABATT_EINVAL;
@@ -152,7 +156,7 @@ abatt_status abatt_key_means(const abatt_problem_t* p, const void* K, float* kme
   Shape s;
   abatt_status st = make_shape(p, &s);
   if (st != ABATT_OK) return st;
-  if (K == nullptr || kmean == nullptr) return ABATT_EINVAL;
+  if (bad(K) || bad(kmean)) return ABATT_EINVAL;
   return hip_status(abatt::launch_key_means(s, K, kmean, stream));
 }
 
@@ -162,7 +166,7 @@ abatt_status abatt_scores(const abatt_problem_t* p, const void* Q, const void* K
   Shape s;
   abatt_status st = make_shape(p, &s);
   if (st != ABATT_OK) return st;
-  if (Q == nullptr || K == nullptr || S == nullptr || workspace == nullptr) return ABATT_EINVAL;
+  if (bad(Q) || bad(K) || S == nullptr || bad(workspace)) return ABATT_EINVAL;
   const PlanWs l = plan_ws_layout(s);
   if (workspace_bytes < l.total) return ABATT_EWORKSPACE;
   char* ws = static_cast<char*>(workspace);
@@ -181,7 +185,7 @@ abatt_status abatt_plan_from_scores(const abatt_problem_t* p, const float* S, do
   Shape s;
   abatt_status st = make_shape(p, &s);
   if (st != ABATT_OK) return st;
-  if (S == nullptr || workspace == nullptr || !budget_ok(budget)) return ABATT_EINVAL;
+  if (S == nullptr || bad(workspace) || !budget_ok(budget)) return ABATT_EINVAL;
   st = check_plan(s, plan, true);
   if (st != ABATT_OK) return st;
   if (workspace_bytes < sampler_ws_bytes(s)) return ABATT_EWORKSPACE;
@@ -197,7 +201,7 @@ abatt_status abatt_plan(const abatt_problem_t* p, const void* Q, const void* K, 
   Shape s;
   abatt_status st = make_shape(p, &s);
   if (st != ABATT_OK) return st;
-  if (Q == nullptr || K == nullptr || workspace == nullptr || !budget_ok(budget))
+  if (bad(Q) || bad(K) || bad(workspace) || !budget_ok(budget))
     return ABATT_EINVAL;
   st = check_plan(s, plan, true);
   if (st != ABATT_OK) return st;
@@ -223,7 +227,7 @@ abatt_status abatt_attend(const abatt_problem_t* p, const void* Q, const void* K
   Shape s;
   abatt_status st = make_shape(p, &s);
   if (st != ABATT_OK) return st;
-  if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr) return ABATT_EINVAL;
+  if (bad(Q) || bad(K) || bad(V) || bad(O)) return ABATT_EINVAL;
   st = check_plan(s, plan, false);
   if (st != ABATT_OK) return st;
   return hip_status(abatt::launch_attend(s, Q, K, V, plan->row_ptr, plan->col_idx, plan->logw,
@@ -237,7 +241,7 @@ abatt_status abatt_v_to_f16(const abatt_problem_t* p, const void* V, void* V16,
   abatt_status st = make_shape(p, &s);
   if (st != ABATT_OK) return st;
   if (!s.bf16) return ABATT_EUNSUPPORTED;
-  if (V == nullptr || V16 == nullptr || V == V16) return ABATT_EINVAL;
+  if (bad(V) || bad(V16) || V == V16) return ABATT_EINVAL;
   return hip_status(abatt::launch_v_to_f16(s, V, V16, stream));
 }
 
@@ -248,7 +252,7 @@ abatt_status abatt_attend_v16(const abatt_problem_t* p, const void* Q, const voi
   abatt_status st = make_shape(p, &s);
   if (st != ABATT_OK) return st;
   if (!s.bf16) return ABATT_EUNSUPPORTED;
-  if (Q == nullptr || K == nullptr || V16 == nullptr || O == nullptr) return ABATT_EINVAL;
+  if (bad(Q) || bad(K) || bad(V16) || bad(O)) return ABATT_EINVAL;
   st = check_plan(s, plan, false);
   if (st != ABATT_OK) return st;
   return hip_status(abatt::launch_attend(s, Q, K, V16, plan->row_ptr, plan->col_idx,
@@ -261,7 +265,7 @@ abatt_status abatt_dense(const abatt_problem_t* p, const void* Q, const void* K,
   Shape s;
   abatt_status st = make_dense_shape(p, &s);
   if (st != ABATT_OK) return st;
-  if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr) return ABATT_EINVAL;
+  if (bad(Q) || bad(K) || bad(V) || bad(O)) return ABATT_EINVAL;
   return hip_status(abatt::launch_attend(s, Q, K, V, nullptr, nullptr, nullptr, 0, nullptr, O,
                                          lse, false, false, stream));
 }

@@ -7,7 +7,8 @@
  *   abatt_attend  Q, K, V, plan   -> O (+ log-sum-exp)
  *   abatt_dense   Q, K, V         -> O (+ log-sum-exp), every key, no shift
  *
- * plus test hooks that enter the same kernels part-way (abatt_key_means,
+ * abatt_v_to_f16 + abatt_attend_v16 split abatt_attend in two (V converted to
+ * fp16 once per call; the same results from a faster kernel), plus test hooks that enter the same kernels part-way (abatt_key_means,
  * abatt_scores, abatt_plan_from_scores).
  *
  * Pages this follows:
@@ -21,6 +22,9 @@
  *     the problem's dtype.  Tokens are in their original (raster) order: the
  *     library never permutes them ([hamidun] three techniques: the clustering
  *     only estimates importance; the computation runs in token order).
+ *   - Q, K, V, O (and V16, kmean and workspaces) are read and written 16
+ *     bytes at a time and must be 16-byte aligned, as every torch allocation
+ *     is; a NULL or misaligned pointer is rejected with ABATT_EINVAL.
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
  *     never allocates or frees device memory and never synchronises: each
  *     call checks its arguments on the host, enqueues kernels on `stream` and

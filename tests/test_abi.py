@@ -115,6 +115,16 @@ def test_argument_checks_before_any_hip_call(lib):
     small = ab._Plan(0x1000, 0x1000, 0x1000, 10, 0x1000)
     wsf = lib.abatt_plan_workspace_bytes(P(pf))
     assert lib.abatt_plan(P(pf), fake, fake, 0.1, 0, fake, wsf, P(small), None) == -4
+    # misaligned tensors or workspace (the kernels move 16 bytes at a time)
+    odd = ctypes.c_void_p(0x1008)
+    assert lib.abatt_plan(P(c), fake, odd, 0.1, 0, fake, ws, P(good), None) == -1
+    assert lib.abatt_plan(P(c), fake, fake, 0.1, 0, odd, ws, P(good), None) == -1
+    assert lib.abatt_attend(P(c), fake, fake, odd, P(good), fake, None, None) == -1
+    assert lib.abatt_attend(P(c), fake, fake, fake, P(good), odd, None, None) == -1
+    assert lib.abatt_dense(P(c), odd, fake, fake, fake, None, None) == -1
+    assert lib.abatt_v_to_f16(P(c), fake, odd, None) == -1
+    assert lib.abatt_attend_v16(P(c), fake, fake, odd, P(good), fake, None, None) == -1
+    assert lib.abatt_key_means(P(c), odd, fake, None) == -1
     # fp16 V: nulls, V16 aliasing V, fp32 problems
     assert lib.abatt_v_to_f16(P(c), None, fake, None) == -1
     assert lib.abatt_v_to_f16(P(c), fake, fake, None) == -1
