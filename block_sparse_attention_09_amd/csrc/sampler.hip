@@ -33,7 +33,8 @@ namespace abatt {
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): per round two 32x32->64
 // multiplies (one v_mad_u64_u32 each), the high halves XORed into the other
-// words with the key, a Weyl key schedule, ten rounds.
+// words with the key (one three-input XOR each), a Weyl key schedule, ten
+// rounds.
 __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
   const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
   const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
@@ -44,8 +45,9 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32
       k1 += W1;
     }
     const uint64_t p0 = (uint64_t)M0 * c[0], p1 = (uint64_t)M1 * c[2];
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    // three-input XORs in one gfx950 v_bitop3_b32 each (truth table 0x96)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c[1], k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c[3], k1, 0x96);
     c[0] = n0;
     c[1] = (uint32_t)p1;
     c[2] = n2;
