@@ -104,6 +104,26 @@ size_t sampler_ws_bytes(const Shape& s) { return align_up(abatt::sampler_ws_layo
 
 abatt_status hip_status(hipError_t e) { return e == hipSuccess ? ABATT_OK : ABATT_EHIP; }
 
+// Key means in their scoring form, centroids and weights, scores.  The
+// key-mean region holds two bf16 planes (fp32 problems) or one fp16 plane
+// followed by the per-tile scales (bf16 problems), which fits in the same
+// space.
+hipError_t run_scores(const Shape& s, const PlanWs& l, char* ws, const void* Q, const void* K,
+                      float* mu, float* w, float* S, hipStream_t stream) {
+  uint16_t* kplanes = reinterpret_cast<uint16_t*>(ws + l.kmean);
+  float* tscale = nullptr;
+  hipError_t e;
+  if (s.bf16) {
+    tscale = reinterpret_cast<float*>(kplanes + (size_t)s.B * s.H * s.n_kbs * s.D);
+    e = abatt::launch_key_means_f16(s, K, kplanes, tscale, stream);
+  } else {
+    e = abatt::launch_key_means_split(s, K, kplanes, stream);
+  }
+  if (e == hipSuccess) e = abatt::launch_kmeans(s, Q, mu, w, stream);
+  if (e == hipSuccess) e = abatt::launch_scores(s, mu, w, kplanes, tscale, S, stream);
+  return e;
+}
+
 bool budget_ok(double budget) { return budget > 0.0 && budget <= 1.0 && std::isfinite(budget); }
 
 abatt_status check_plan(const Shape& s, const abatt_plan_t* plan, bool need_status) {
@@ -170,13 +190,9 @@ abatt_status abatt_scores(const abatt_problem_t* p, const void* Q, const void* K
   const PlanWs l = plan_ws_layout(s);
   if (workspace_bytes < l.total) return ABATT_EWORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  uint16_t* kplanes = reinterpret_cast<uint16_t*>(ws + l.kmean);
   float* mu = centroids ? centroids : reinterpret_cast<float*>(ws + l.mu);
   float* w = weights ? weights : reinterpret_cast<float*>(ws + l.w);
-  hipError_t e = abatt::launch_key_means_split(s, K, kplanes, stream);
-  if (e == hipSuccess) e = abatt::launch_kmeans(s, Q, mu, w, stream);
-  if (e == hipSuccess) e = abatt::launch_scores(s, mu, w, kplanes, S, stream);
-  return hip_status(e);
+  return hip_status(run_scores(s, l, ws, Q, K, mu, w, S, stream));
 }
 
 abatt_status abatt_plan_from_scores(const abatt_problem_t* p, const float* S, double budget,
@@ -209,13 +225,10 @@ abatt_status abatt_plan(const abatt_problem_t* p, const void* Q, const void* K, 
   if (workspace_bytes < l.total) return ABATT_EWORKSPACE;
   if (plan->capacity < (int64_t)s.R * (s.n_kb - s.n_kbs)) return ABATT_ECAPACITY;
   char* ws = static_cast<char*>(workspace);
-  uint16_t* kplanes = reinterpret_cast<uint16_t*>(ws + l.kmean);
   float* mu = reinterpret_cast<float*>(ws + l.mu);
   float* w = reinterpret_cast<float*>(ws + l.w);
   float* S = reinterpret_cast<float*>(ws + l.S);
-  hipError_t e = abatt::launch_key_means_split(s, K, kplanes, stream);
-  if (e == hipSuccess) e = abatt::launch_kmeans(s, Q, mu, w, stream);
-  if (e == hipSuccess) e = abatt::launch_scores(s, mu, w, kplanes, S, stream);
+  hipError_t e = run_scores(s, l, ws, Q, K, mu, w, S, stream);
   if (e == hipSuccess)
     e = abatt::launch_sampler(s, S, budget, seed, ws + l.sampler, plan->row_ptr, plan->col_idx,
                               plan->logw, plan->capacity, plan->status, stream);

@@ -19,17 +19,22 @@ struct Shape {
   bool bf16;     // dtype of Q/K/V/O
 };
 
-// key_means.hip: fp32 means [B,H,n_kbs,D], or the same means as two bf16
-// planes (hi then lo, each [B,H,n_kbs,D]) for the scoring MFMAs
+// key_means.hip: fp32 means [B,H,n_kbs,D]; for the scorer either the same
+// means as two bf16 planes (hi then lo, each [B,H,n_kbs,D]; fp32 problems) or
+// (bf16 problems) one fp16 plane [B,H,n_kbs,D] scaled per 32-block tile, with
+// the tiles' scales [B,H,ceil(n_kbs/32)] in tscale
 hipError_t launch_key_means(const Shape& s, const void* K, float* kmean, hipStream_t st);
 hipError_t launch_key_means_split(const Shape& s, const void* K, uint16_t* planes, hipStream_t st);
+hipError_t launch_key_means_f16(const Shape& s, const void* K, uint16_t* kh, float* tscale,
+                                hipStream_t st);
 
 // kmeans.hip: centroids [R, C, D] fp32 and weights [R, C] fp32
 hipError_t launch_kmeans(const Shape& s, const void* Q, float* mu, float* w, hipStream_t st);
 
-// score.hip: S [R, n_kbs] fp32 from centroids, weights and the split key means
+// score.hip: S [R, n_kbs] fp32 from centroids, weights and the key means in
+// their scoring form (split planes, tscale null; or the scaled fp16 plane)
 hipError_t launch_scores(const Shape& s, const float* mu, const float* w, const uint16_t* kplanes,
-                         float* S, hipStream_t st);
+                         const float* tscale, float* S, hipStream_t st);
 
 // sampler.hip: counts -> row_ptr -> col_idx/logw.  The sampler's scratch
 // (row counts, kept-block bitmasks, per-row solves) lives in `ws`.

@@ -12,6 +12,40 @@
 
 namespace abatt {
 
+// Mean of dims 8c..8c+7 of one bf16 key block whose first row is `src`.
+template <int D>
+__device__ __forceinline__ void block_mean8_bf16(const uint16_t* __restrict__ src, int kb,
+                                                 float (&out)[8]) {
+  if (kb == 4) {
+    u32x4 r0 = *reinterpret_cast<const u32x4*>(src);
+    u32x4 r1 = *reinterpret_cast<const u32x4*>(src + D);
+    u32x4 r2 = *reinterpret_cast<const u32x4*>(src + 2 * D);
+    u32x4 r3 = *reinterpret_cast<const u32x4*>(src + 3 * D);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a0 = bf16_bits_to_f32(r0[e] & 0xffffu), b0 = bf16_bits_to_f32(r0[e] >> 16);
+      const float a1 = bf16_bits_to_f32(r1[e] & 0xffffu), b1 = bf16_bits_to_f32(r1[e] >> 16);
+      const float a2 = bf16_bits_to_f32(r2[e] & 0xffffu), b2 = bf16_bits_to_f32(r2[e] >> 16);
+      const float a3 = bf16_bits_to_f32(r3[e] & 0xffffu), b3 = bf16_bits_to_f32(r3[e] >> 16);
+      out[2 * e] = (((a0 + a1) + a2) + a3) * 0.25f;
+      out[2 * e + 1] = (((b0 + b1) + b2) + b3) * 0.25f;
+    }
+  } else {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int tk = 0; tk < kb; ++tk) {
+      const u32x4 rr = *reinterpret_cast<const u32x4*>(src + (int64_t)tk * D);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += bf16_bits_to_f32(rr[e] & 0xffffu);
+        acc[2 * e + 1] += bf16_bits_to_f32(rr[e] >> 16);
+      }
+    }
+    const float inv = 1.f / (float)kb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = acc[e] * inv;
+  }
+}
+
 // bf16 input: one thread = 8 dims of one block (4 x 16-byte loads).  Writes
 // either the fp32 means or (kSplit) the means as two bf16 planes hi + lo with
 // hi = bf16(mean), lo = bf16(mean - hi): the operands of the split-bf16
@@ -28,36 +62,8 @@ __global__ __launch_bounds__(256) void k_key_means_bf16(const uint16_t* __restri
     const int64_t bj = i / CH;  // bh * n_kbs + j
     const int j = (int)(bj % n_kbs);
     const int64_t bh = bj / n_kbs;
-    const uint16_t* src = K + (bh * N + (int64_t)kb * j) * D + 8 * c;
     float out[8];
-    if (kb == 4) {
-      u32x4 r0 = *reinterpret_cast<const u32x4*>(src);
-      u32x4 r1 = *reinterpret_cast<const u32x4*>(src + D);
-      u32x4 r2 = *reinterpret_cast<const u32x4*>(src + 2 * D);
-      u32x4 r3 = *reinterpret_cast<const u32x4*>(src + 3 * D);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float a0 = bf16_bits_to_f32(r0[e] & 0xffffu), b0 = bf16_bits_to_f32(r0[e] >> 16);
-        const float a1 = bf16_bits_to_f32(r1[e] & 0xffffu), b1 = bf16_bits_to_f32(r1[e] >> 16);
-        const float a2 = bf16_bits_to_f32(r2[e] & 0xffffu), b2 = bf16_bits_to_f32(r2[e] >> 16);
-        const float a3 = bf16_bits_to_f32(r3[e] & 0xffffu), b3 = bf16_bits_to_f32(r3[e] >> 16);
-        out[2 * e] = (((a0 + a1) + a2) + a3) * 0.25f;
-        out[2 * e + 1] = (((b0 + b1) + b2) + b3) * 0.25f;
-      }
-    } else {
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int tk = 0; tk < kb; ++tk) {
-        const u32x4 rr = *reinterpret_cast<const u32x4*>(src + (int64_t)tk * D);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += bf16_bits_to_f32(rr[e] & 0xffffu);
-          acc[2 * e + 1] += bf16_bits_to_f32(rr[e] >> 16);
-        }
-      }
-      const float inv = 1.f / (float)kb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = acc[e] * inv;
-    }
+    block_mean8_bf16<D>(K + (bh * N + (int64_t)kb * j) * D + 8 * c, kb, out);
     if constexpr (kSplit) {
       uint16_t* hi = reinterpret_cast<uint16_t*>(kmean);
       uint16_t* lo = hi + total * 8;
@@ -130,6 +136,65 @@ __global__ __launch_bounds__(256) void k_key_means_f32(const float* __restrict__
   }
 }
 
+// bf16 input, the scoring form for bf16 problems: the means of one tile of
+// 32 consecutive blocks of a head (the scorer's tile) as fp16 values scaled
+// by 2^-e, with e chosen so that the tile's largest magnitude lands in
+// [2^14, 2^15), and 2^e in tscale[head tile].  A power-of-two scale is exact,
+// so every mean keeps fp16's 11 significant bits whatever the keys' range (no
+// overflow; underflow only for values 2^-28 below the tile's largest).
+// One work-group per (head, tile); a thread holds 8 dims of 1 (D = 64) or 2
+// (D = 128) blocks, reduces the tile's largest |mean| with the others, then
+// scales, rounds to nearest and stores.
+template <int D>
+__global__ __launch_bounds__(256) void k_key_means_f16(const uint16_t* __restrict__ K,
+                                                       uint16_t* __restrict__ kh,
+                                                       float* __restrict__ tscale, int N,
+                                                       int n_kbs, int n_tiles, int kb) {
+  constexpr int CH = D / 8;
+  constexpr int NI = 32 * CH / 256;  // blocks-by-chunk items per thread
+  static_assert(NI * 256 == 32 * CH, "one tile = whole items per thread");
+  __shared__ float red[4];
+  const int t = threadIdx.x;
+  const int tile = (int)(blockIdx.x % (unsigned)n_tiles);
+  const int64_t bh = blockIdx.x / (unsigned)n_tiles;
+  float out[NI][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int q = ii * 256 + t;
+    const int key = 32 * tile + q / CH, c = q % CH;
+    if (key < n_kbs) {
+      block_mean8_bf16<D>(K + (bh * N + (int64_t)kb * key) * D + 8 * c, kb, out[ii]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[ii][e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(out[ii][e]));
+  }
+  amax = wave_max(amax);
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  // m = f * 2^x with f in [0.5, 1): m * 2^-(x - 15) lies in [2^14, 2^15)
+  int e = m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 15 : 0;
+  e = e < -126 ? -126 : (e > 127 ? 127 : e);
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int q = ii * 256 + t;
+    const int key = 32 * tile + q / CH, c = q % CH;
+    if (key < n_kbs) {
+      u32x4 h;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        h[v] = pack_f16_rne(__builtin_amdgcn_ldexpf(out[ii][2 * v], -e),
+                            __builtin_amdgcn_ldexpf(out[ii][2 * v + 1], -e));
+      *reinterpret_cast<u32x4*>(kh + (bh * n_kbs + key) * D + 8 * c) = h;
+    }
+  }
+  if (t == 0) tscale[blockIdx.x] = __builtin_amdgcn_ldexpf(1.f, e);
+}
+
 template <bool kSplit>
 static hipError_t launch_means(const Shape& s, const void* K, float* out, hipStream_t st) {
   const int64_t blocks = (int64_t)s.B * s.H * s.n_kbs;
@@ -160,6 +225,19 @@ hipError_t launch_key_means(const Shape& s, const void* K, float* kmean, hipStre
 
 hipError_t launch_key_means_split(const Shape& s, const void* K, uint16_t* planes, hipStream_t st) {
   return launch_means<true>(s, K, reinterpret_cast<float*>(planes), st);
+}
+
+hipError_t launch_key_means_f16(const Shape& s, const void* K, uint16_t* kh, float* tscale,
+                                hipStream_t st) {
+  const int n_tiles = (s.n_kbs + 31) / 32;
+  const int64_t grid = (int64_t)s.B * s.H * n_tiles;
+  if (s.D == 128)
+    k_key_means_f16<128><<<(unsigned)grid, 256, 0, st>>>((const uint16_t*)K, kh, tscale, s.N,
+                                                         s.n_kbs, n_tiles, s.kv_block);
+  else
+    k_key_means_f16<64><<<(unsigned)grid, 256, 0, st>>>((const uint16_t*)K, kh, tscale, s.N,
+                                                        s.n_kbs, n_tiles, s.kv_block);
+  return hipGetLastError();
 }
 
 }  // namespace abatt

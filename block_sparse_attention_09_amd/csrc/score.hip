@@ -8,17 +8,25 @@
 //
 // One work-group holds 256 centroid rows (256/C query blocks of one head) and
 // streams that head's key means twice, 32 blocks per tile, through LDS (the
-// means arrive as bf16 hi and lo planes written by the key-means kernel):
+// means arrive in their scoring form, written by the key-means kernel):
 //   pass 1: per-centroid running max and sum of exp2 (the softmax normaliser);
 //   pass 2: p = exp2(logit + log2 w_c - lse_c), summed over the C centroids of
 //           each query block and written to S.
-// The dot products run on bf16 MFMA with both operands split into bf16 high
-// and low parts (hi*hi + hi*lo + lo*hi, fp32 accumulation), which keeps the
-// logits within ~2^-16 relative of fp32.  Pass 1 uses the key means as the
-// MFMA A operand (a lane then holds 16 keys of one centroid: cheap running
-// max), pass 2 uses the centroids as A (a lane holds 16 centroids of one key:
-// cheap sum over a query block's centroids).  The operand registers are the
-// same in both layouts.
+// Two precisions of the dot products, both accumulated in fp32:
+//   * bf16 problems (kF16): one fp16 MFMA per k-step.  The key means come as
+//     fp16 scaled by a power of two per tile, the centroids are scaled by one
+//     power of two per work-group, both so that their largest magnitude lies
+//     in [2^14, 2^15): no overflow, 11 significant bits (finer than the bf16
+//     keys and queries they are averaged from).  The two scales multiply the
+//     logit inside the fma that already subtracts the running max (pass 1)
+//     or adds the centroid's offset (pass 2).
+//   * fp32 problems: both operands split into bf16 high and low parts
+//     (hi*hi + hi*lo + lo*hi, three MFMAs per k-step), which keeps the logits
+//     within ~2^-16 relative of fp32.
+// Pass 1 uses the key means as the MFMA A operand (a lane then holds 16 keys
+// of one centroid: cheap running max), pass 2 uses the centroids as A (a lane
+// holds 16 centroids of one key: cheap sum over a query block's centroids).
+// The operand registers are the same in both layouts.
 //
 // Each pass is software-pipelined: the MFMAs of tile t+1 are issued in the
 // same block as the exp2 work of tile t, so the matrix core and the vector
@@ -32,10 +40,11 @@ constexpr int kScoreWaves = 8;                 // 256 centroid rows per work-gro
 constexpr int kScoreT = 64 * kScoreWaves;
 constexpr int kScoreStages = 3;                // LDS ring of key-mean tiles
 
-template <int D, int C>
+template <int D, int C, bool kF16>
 __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__ mu,
                                                        const float* __restrict__ w,
                                                        const uint16_t* __restrict__ kplanes,
+                                                       const float* __restrict__ tscale,
                                                        float* __restrict__ S, int n_qb, int n_kbs,
                                                        int groups_per_head, int n_groups,
                                                        int64_t plane_elems, float scale_log2) {
@@ -46,7 +55,10 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
   constexpr int CH = D / 8;               // 16-byte chunks per key-mean row
   constexpr int TILE_CH = 32 * CH;        // chunks per plane per 32-key tile
   constexpr int NCH = (TILE_CH + kScoreT - 1) / kScoreT;  // per thread per plane
-  __shared__ __align__(16) uint16_t ring[kScoreStages][2][32 * ROWB];
+  constexpr int NP = kF16 ? 1 : 2;                         // planes of key means
+  __shared__ __align__(16) uint16_t ring[kScoreStages][NP][32 * ROWB];
+  __shared__ float tsc[kScoreStages];  // scale of the tile in each stage (kF16)
+  __shared__ float red[kScoreWaves];
   __shared__ float a_lds[ROWS];
 
   const int gid = xcd_remap(blockIdx.x, n_groups);
@@ -76,25 +88,26 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
   const uint16_t* lbase = hbase + plane_elems;
   const int n_tiles = (n_kbs + 31) / 32;
   const int tlast = n_tiles - 1;
+  const float* tsbase = kF16 ? tscale + (int64_t)bh * n_tiles : nullptr;
 
   auto kop = [&](const uint16_t* base, int s) -> u32x4 {
     return *reinterpret_cast<const u32x4*>(base + l32 * ROWB + 16 * s + 8 * hh);
   };
 
-  // One pipelined pass over the planes p0 and p1.  Tile t sits in LDS
-  // stage t%3.  Two register sets alternate (the loop is unrolled by two so
+  // One pipelined pass over the planes p0 and p1 (p0 only with kF16, and
+  // the tile's scale with it).  Tile t sits in LDS stage t%3.  Two register sets alternate (the loop is unrolled by two so
   // they stay in registers): the set holding tile t+2 goes to stage (t+2)%3
   // at the top of the half-iteration for tile t and is reloaded with tile
   // t+4, so every load has two half-iterations to land.  `mma(stage)` forms
   // a tile's logits from LDS, `fix(x, tile)` masks keys past the end (a
-  // small block of its own), `epi(x, tile)` consumes them; mma of tile t+1
+  // small block of its own), `epi(x, tile, stage)` consumes them; mma of tile t+1
   // runs in the half-iteration of tile t (stage (t+1)%3 was stored before the
   // previous barrier, and stage (t+2)%3 was last read one half-iteration
   // earlier still).
   auto run_pass = [&](const uint16_t* p0, const uint16_t* p1, auto&& mma, auto&& fix, auto&& epi) {
-    constexpr int NP = 2;
     struct Regs {
       u32x4 v[NP][NCH];
+      float sc;
     };
     Regs ra, rb;
     auto load_tile = [&](Regs& r, int tile) {
@@ -106,9 +119,10 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
         const int64_t off = (int64_t)key * D + 8 * (q % CH);
         if (q < TILE_CH) {
           r.v[0][i] = *reinterpret_cast<const u32x4*>(p0 + off);
-          r.v[1][i] = *reinterpret_cast<const u32x4*>(p1 + off);
+          if constexpr (NP == 2) r.v[1][i] = *reinterpret_cast<const u32x4*>(p1 + off);
         }
       }
+      if constexpr (kF16) r.sc = tsbase[tile];
     };
     auto store_tile = [&](const Regs& r, int stage) {
 #pragma unroll
@@ -120,6 +134,8 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
           for (int pl = 0; pl < NP; ++pl) *reinterpret_cast<u32x4*>(&ring[stage][pl][o]) = r.v[pl][i];
         }
       }
+      if constexpr (kF16)
+        if (t == 0) tsc[stage] = r.sc;
     };
     load_tile(ra, 0);
     store_tile(ra, 0);
@@ -139,30 +155,60 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
       load_tile(ra, min(tile + 4, tlast));
       fix(xa, tile);
       xb = mma(s1);
-      epi(xa, tile);
+      epi(xa, tile, st);
       __syncthreads();
       if (tile + 1 < n_tiles) {
         store_tile(rb, st);  // stage of tile + 3
         load_tile(rb, min(tile + 5, tlast));
         fix(xb, tile + 1);
         xa = mma(s2);
-        epi(xb, tile + 1);
+        epi(xb, tile + 1, s1);
         __syncthreads();
       }
       st = s2;
     }
   };
 
-  bf16x8 mh[KS], ml[KS];
+  // centroid operands: bf16 hi/lo (fp32 problems) or fp16 scaled by 2^-e_mu
+  // (bf16 problems; e_mu from the work-group's largest |scale_log2 * mu|)
+  constexpr int KH = kF16 ? 1 : KS;
+  bf16x8 mh[KH], ml[KH];
+  f16x8 m16[kF16 ? KS : 1];
+  float fac_mu = 1.f;  // 2^e_mu
+  if constexpr (kF16) {
+    float x[KS][8];
+    float amax = 0.f;
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    float x[8];
-    mu_slice(s, x);
+    for (int s = 0; s < KS; ++s) {
+      mu_slice(s, x[s]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const __bf16 hb = (__bf16)x[i];
-      mh[s][i] = hb;
-      ml[s][i] = (__bf16)(x[i] - (float)hb);
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[s][i]));
+    }
+    amax = wave_max(amax);
+    if (lane == 0) red[wv] = amax;
+    __syncthreads();
+    float m = red[0];
+#pragma unroll
+    for (int i = 1; i < kScoreWaves; ++i) m = fmaxf(m, red[i]);
+    // m = f * 2^x with f in [0.5, 1): m * 2^-(x - 15) lies in [2^14, 2^15)
+    int e = m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 15 : 0;
+    e = e < -126 ? -126 : (e > 127 ? 127 : e);
+    fac_mu = __builtin_amdgcn_ldexpf(1.f, e);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m16[s][i] = (_Float16)__builtin_amdgcn_ldexpf(x[s][i], -e);
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float x[8];
+      mu_slice(s, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const __bf16 hb = (__bf16)x[i];
+        mh[s][i] = hb;
+        ml[s][i] = (__bf16)(x[i] - (float)hb);
+      }
     }
   }
 
@@ -170,18 +216,24 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
   float m_run = -INFINITY, s_run = 0.f;
   {
     auto mma1 = [&](int stage) {
-      // one accumulation chain: the small cross terms first, then hi*hi
       f32x16 x = {};
+      if constexpr (kF16) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 kh = __builtin_bit_cast(bf16x8, kop(ring[stage][0], s));
-        const bf16x8 kl = __builtin_bit_cast(bf16x8, kop(ring[stage][1], s));
-        x = mfma_bf16_32x32x16(kl, mh[s], x);
-        x = mfma_bf16_32x32x16(kh, ml[s], x);
+        for (int s = 0; s < KS; ++s)
+          x = mfma_f16_32x32x16(__builtin_bit_cast(f16x8, kop(ring[stage][0], s)), m16[s], x);
+      } else {
+        // one accumulation chain: the small cross terms first, then hi*hi
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 kh = __builtin_bit_cast(bf16x8, kop(ring[stage][0], s));
+          const bf16x8 kl = __builtin_bit_cast(bf16x8, kop(ring[stage][NP - 1], s));
+          x = mfma_bf16_32x32x16(kl, mh[s], x);
+          x = mfma_bf16_32x32x16(kh, ml[s], x);
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          x = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, kop(ring[stage][0], s)), mh[s], x);
       }
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        x = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, kop(ring[stage][0], s)), mh[s], x);
       return x;
     };
     auto fix1 = [&](f32x16& x, int tile) {
@@ -193,17 +245,19 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
           if (32 * tile + 8 * (v >> 2) + 4 * hh + (v & 3) >= n_kbs) x[v] = -INFINITY;
       }
     };
-    auto epi1 = [&](const f32x16& x, int tile) {
+    auto epi1 = [&](const f32x16& x, int, int stage) {
+      // logit = fac * x, fac a positive power of two (1 for split operands)
+      const float fac = kF16 ? tsc[stage] * fac_mu : 1.f;
       float tmax = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, x[v]);
       const f32x2 tp = pair_x32(tmax);
-      tmax = fmaxf(tp[0], tp[1]);  // finite: every tile has a valid key
+      tmax = fmaxf(tp[0], tp[1]) * fac;  // finite: every tile has a valid key
       const float m_new = fmaxf(m_run, tmax);
       s_run *= __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s_run += __builtin_amdgcn_exp2f(x[v] - m_run);
+      for (int v = 0; v < 16; ++v) s_run += __builtin_amdgcn_exp2f(fmaf(x[v], fac, -m_run));
     };
     run_pass(hbase, lbase, mma1, fix1, epi1);
   }
@@ -231,26 +285,33 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), srs, off, 0, 0);
   };
   auto mma2 = [&](int stage) {
-    // one accumulation chain: the small cross terms first, then hi*hi
     f32x16 x = {};
+    if constexpr (kF16) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 kh = __builtin_bit_cast(bf16x8, kop(ring[stage][0], s));
-      const bf16x8 kl = __builtin_bit_cast(bf16x8, kop(ring[stage][1], s));
-      x = mfma_bf16_32x32x16(mh[s], kl, x);
-      x = mfma_bf16_32x32x16(ml[s], kh, x);
+      for (int s = 0; s < KS; ++s)
+        x = mfma_f16_32x32x16(m16[s], __builtin_bit_cast(f16x8, kop(ring[stage][0], s)), x);
+    } else {
+      // one accumulation chain: the small cross terms first, then hi*hi
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 kh = __builtin_bit_cast(bf16x8, kop(ring[stage][0], s));
+        const bf16x8 kl = __builtin_bit_cast(bf16x8, kop(ring[stage][NP - 1], s));
+        x = mfma_bf16_32x32x16(mh[s], kl, x);
+        x = mfma_bf16_32x32x16(ml[s], kh, x);
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        x = mfma_bf16_32x32x16(mh[s], __builtin_bit_cast(bf16x8, kop(ring[stage][0], s)), x);
     }
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      x = mfma_bf16_32x32x16(mh[s], __builtin_bit_cast(bf16x8, kop(ring[stage][0], s)), x);
     return x;
   };
   auto fix2 = [](f32x16&, int) {};
-  auto epi2 = [&](const f32x16& x, int tile) {
+  auto epi2 = [&](const f32x16& x, int tile, int stage) {
     // lane: key 32*tile + l32, centroid rows 32*wv + 8*(v/4) + 4*hh + v%4
+    const float fac = kF16 ? tsc[stage] * fac_mu : 1.f;
     float p[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(x[v] + a_v[v]);
+    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(x[v], fac, a_v[v]));
     const int key = 32 * tile + l32;
     if constexpr (C == 8) {
       // rows 8g..8g+7 of the wave = one query block; this half holds 4 of them
@@ -283,23 +344,29 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
 
 template <int D, int C>
 static hipError_t launch_scores_t(const Shape& s, const float* mu, const float* w,
-                                  const uint16_t* kplanes, float* S, hipStream_t st) {
+                                  const uint16_t* kplanes, const float* tscale, float* S,
+                                  hipStream_t st) {
   constexpr int G = 32 * kScoreWaves / C;
   const int gph = (s.n_qb + G - 1) / G;
   const int n_groups = s.B * s.H * gph;
   const int64_t plane = (int64_t)s.B * s.H * s.n_kbs * s.D;
-  k_scores<D, C><<<n_groups, kScoreT, 0, st>>>(mu, w, kplanes, S, s.n_qb, s.n_kbs, gph, n_groups,
-                                           plane, s.scale * kLog2e);
+  if (s.bf16)
+    k_scores<D, C, true><<<n_groups, kScoreT, 0, st>>>(mu, w, kplanes, tscale, S, s.n_qb, s.n_kbs,
+                                                       gph, n_groups, plane, s.scale * kLog2e);
+  else
+    k_scores<D, C, false><<<n_groups, kScoreT, 0, st>>>(mu, w, kplanes, nullptr, S, s.n_qb,
+                                                        s.n_kbs, gph, n_groups, plane,
+                                                        s.scale * kLog2e);
   return hipGetLastError();
 }
 
 hipError_t launch_scores(const Shape& s, const float* mu, const float* w, const uint16_t* kplanes,
-                         float* S, hipStream_t st) {
+                         const float* tscale, float* S, hipStream_t st) {
   if (s.D == 128)
-    return s.n_clusters == 8 ? launch_scores_t<128, 8>(s, mu, w, kplanes, S, st)
-                             : launch_scores_t<128, 16>(s, mu, w, kplanes, S, st);
-  return s.n_clusters == 8 ? launch_scores_t<64, 8>(s, mu, w, kplanes, S, st)
-                           : launch_scores_t<64, 16>(s, mu, w, kplanes, S, st);
+    return s.n_clusters == 8 ? launch_scores_t<128, 8>(s, mu, w, kplanes, tscale, S, st)
+                             : launch_scores_t<128, 16>(s, mu, w, kplanes, tscale, S, st);
+  return s.n_clusters == 8 ? launch_scores_t<64, 8>(s, mu, w, kplanes, tscale, S, st)
+                           : launch_scores_t<64, 16>(s, mu, w, kplanes, tscale, S, st);
 }
 
 }  // namespace abatt

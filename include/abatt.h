@@ -120,7 +120,10 @@ size_t abatt_sampler_workspace_bytes(const abatt_problem_t *p);
  *      the evenly spaced members, kmeans_iters iterations); weight of a
  *      cluster = share of the block's queries in it;
  *   3. score s_j = sum_c w_c softmax_j(scale * mu_c . kmean_j) over the
- *      sparse key blocks, stored as fp32;
+ *      sparse key blocks, stored as fp32.  The dot products take fp16
+ *      operands, scaled by powers of two so that any finite input keeps 11
+ *      significant bits (bf16 problems), or bf16 hi + lo splits of both
+ *      operands (fp32 problems); accumulation and softmax are fp32;
  *   4. inclusion probability pi_j proportional to s_j, capped at 1, summing
  *      to m = budget * n_kbs per row (float64 water-filling);
  *   5. block j kept iff the 53-bit uniform made of words 2(j%2) (32 bits)

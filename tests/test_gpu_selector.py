@@ -63,6 +63,26 @@ def test_centroids_and_scores(name):
     np.testing.assert_allclose(S.sum(axis=1), 1.0, rtol=1e-4)
 
 
+@pytest.mark.parametrize("name", ["tiny_f32", "bf16_ragged", "bf16_d64_b2"])
+@pytest.mark.parametrize("k2", [-30, 30])
+def test_scores_invariant_under_power_of_two_key_scaling(name, k2):
+    # K * 2^k2 with the softmax scale * 2^-k2 gives the same logits.  The
+    # scorer's operands are scaled by powers of two only (per tile of key
+    # means and per work-group of centroids, or bf16 hi/lo splits), so the
+    # scores must come out bit for bit the same, also with |K| near 1e9 or
+    # 1e-9 (far outside fp16's range)
+    wl = SEL[name]
+    q, k, _ = make_qkv(wl)
+    s0 = 1.0 / np.sqrt(wl.D)
+    say(f"scores {name} with K * 2^{k2}")
+    dq = to_dev(q, wl.dtype)
+    S0, _, _ = ab.scores(dq, to_dev(k, wl.dtype), lib_problem(wl, scale=s0))
+    S1, _, _ = ab.scores(dq, to_dev(np.ldexp(k, k2), wl.dtype),
+                         lib_problem(wl, scale=float(np.ldexp(s0, -k2))))
+    torch.cuda.synchronize()
+    assert torch.equal(S0, S1)
+
+
 SAMPLER = [
     # (problem kwargs, budget, score spread, rows checked)
     (dict(B=1, H=2, N=1024, D=64), 0.10, 3.0, None),
