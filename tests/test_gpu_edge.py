@@ -29,10 +29,12 @@ pytestmark = pytest.mark.gpu
 
 ab = pytest.importorskip("block_sparse_attention_09_amd")
 
-# logw = -log(pi) with pi proportional to the score: these plans use the
-# GPU's own scores (agreeing to ~1e-6 relative here), and a relative score
-# error e moves logw by about e in absolute terms
-LOGW_ATOL = 1e-5
+# logw = -log(pi) with pi = c * s_j: these plans use the GPU's own scores, and
+# a relative score error e moves logw by about e in absolute terms, once
+# through s_j and once through the water-filling constant c (a ratio of the
+# row's scores).  So logw's bar is twice the scores' relative bar: 2e-3 for
+# bf16 problems (fp16 operands), ~5e-6 for fp32 problems (split-bf16)
+LOGW_ATOL = {"bf16": 4e-3, "f32": 1e-5}
 
 
 def _plan_and_attend(wl, budget, seed=0):
@@ -58,7 +60,7 @@ def test_tiny_sequences(N, dtype, D, C):
     rp, ci, lw = plan_to_host(pl)
     np.testing.assert_array_equal(rp, ref.row_ptr)
     np.testing.assert_array_equal(ci, ref.col_idx)
-    np.testing.assert_allclose(lw, ref.logw, rtol=0, atol=LOGW_ATOL)
+    np.testing.assert_allclose(lw, ref.logw, rtol=0, atol=LOGW_ATOL[dtype])
     check_output(o, O, dtype, f"tiny N={N} {dtype} C={C}")
     fin = np.isfinite(L)
     assert np.array_equal(np.isfinite(lse.cpu().numpy()), fin)
@@ -99,7 +101,7 @@ def test_budget_below_one_block(dtype, D):
     rp, ci, lw = plan_to_host(pl)
     np.testing.assert_array_equal(rp, ref.row_ptr)
     np.testing.assert_array_equal(ci, ref.col_idx)
-    np.testing.assert_allclose(lw, ref.logw, rtol=0, atol=LOGW_ATOL)
+    np.testing.assert_allclose(lw, ref.logw, rtol=0, atol=LOGW_ATOL[dtype])
     empty = np.diff(ref.row_ptr) == 0
     say(f"  {int(empty.sum())} of {len(empty)} rows empty")
     assert empty.any() and not empty.all()
