@@ -162,3 +162,22 @@ def test_fullsize_stress_plan_reuse():
     lw = pl.logw[: int(rp[-1])].cpu().numpy()
     check_rows("stress call 3", q3, k3, v3, op, rows,
                [ci[rp[r]:rp[r + 1]] for r in rows], [lw[rp[r]:rp[r + 1]] for r in rows], o)
+
+
+@pytest.mark.parametrize("pe_amp", [2.0, 3.0])
+def test_sharp_inputs_plan_attend(pe_amp):
+    """Sharper attention (position code amplitude 2 and 3): the logits spread
+    wider, so the scorer's fp16 products err more in relative terms; the plan
+    still has to agree with the oracle's (>= 99%) and attention to hold its bar."""
+    wl = CONFIGS["wan1p3b_480p"].scaled(H=2, pe_amp=pe_amp)
+    say(f"wan1p3b_480p H=2 pe_amp={pe_amp}: generating inputs")
+    gen, q, k, v, _, _ = gpu_inputs(wl)
+    prob, op = problems(wl)
+    q2, k2, v2 = make_qkv(wl, heads=2)
+    budget = 0.10
+    pl = ab.plan(q, k, budget, seed=wl.plan_seed, problem=prob)
+    o = ab.attend(q, k, v, pl, problem=prob)
+    torch.cuda.synchronize()
+    assert pl.ok()
+    check_plan_and_attend(f"pe_amp {pe_amp}", wl, budget, wl.plan_seed, q2, k2, v2,
+                          q, k, v, prob, op, pl, o)
