@@ -57,7 +57,7 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32
 
 constexpr int kSampT = 512;
 constexpr int kSampWaves = kSampT / 64;
-constexpr double kTwo53 = 9007199254740992.0;
+constexpr double kTwo32 = 4294967296.0;
 
 struct Red {
   double d[kSampWaves];
@@ -216,10 +216,24 @@ __device__ __forceinline__ const float* stage_row(const float* g, int n, float* 
   }
 }
 
+// pi_j * 2^32, exactly: pi_of scaled by a power of two (c32 = c * 2^32, and
+// a power-of-two factor commutes with the product's rounding).
+__device__ __forceinline__ double pi_x32(float s, const PiSolve& ps, double c32) {
+  if (ps.mode == 0) return kTwo32;
+  if (!(s > 0.f)) return 0.0;
+  if (ps.mode == 1 || s >= ps.theta) return kTwo32;
+  return c32 * (double)s;
+}
+
 // Kept-bit mask (4 bits) of blocks 4g..4g+3: two Philox calls (counters 2g
-// and 2g+1), each giving two 53-bit uniforms (words 0,1 and 2,3).
+// and 2g+1), each giving two 53-bit uniforms u = w0 * 2^21 + (w1 >> 11)
+// (words 0,1 and 2,3); kept iff u < pi * 2^53.  With x = pi * 2^32 and
+// f = floor(min(x, 2^32 - 1)), w0 < f implies u < (w0 + 1) * 2^21 <= pi * 2^53
+// and w0 > f implies u >= (f + 1) * 2^21 > pi * 2^53 (for pi < 1; pi = 1
+// gives f = 2^32 - 1 and no w0 above it), so only w0 == f (probability 2^-32)
+// needs the 53-bit compare.
 __device__ __forceinline__ uint32_t draw_group(const float* s, int n, int g, int qb, int h, int b,
-                                               uint64_t seed, const PiSolve& ps) {
+                                               uint64_t seed, const PiSolve& ps, double c32) {
   uint32_t mask = 0;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -229,9 +243,15 @@ __device__ __forceinline__ uint32_t draw_group(const float* s, int n, int g, int
     for (int k = 0; k < 2; ++k) {
       const int j = 4 * g + 2 * i + k;
       if (j < n) {
-        const double pi = pi_of(s[j], ps);
-        const double u = (double)(((uint64_t)c[2 * k] << 21) | (c[2 * k + 1] >> 11));
-        if (u < pi * kTwo53) mask |= 1u << (2 * i + k);
+        const double x = pi_x32(s[j], ps, c32);
+        const uint32_t w0 = c[2 * k];
+        const uint32_t f = x < 4294967295.0 ? (uint32_t)x : 0xffffffffu;
+        bool keep = w0 < f;
+        if (w0 == f) {
+          const double u = (double)(((uint64_t)w0 << 21) | (c[2 * k + 1] >> 11));
+          keep = u < x * 2097152.0;
+        }
+        if (keep) mask |= 1u << (2 * i + k);
       }
     }
   }
@@ -252,6 +272,7 @@ __global__ __launch_bounds__(kSampT) void k_sip_count(const float* __restrict__ 
   RowStats st;
   const float* s = stage_row<kLds>(S + (int64_t)r * n, n, srow, st);
   const PiSolve ps = solve_pi(s, n, budget, st, red);
+  const double c32 = ps.c * kTwo32;
   const int groups = (n + 3) / 4;
   const int words = (n + 31) / 32;
   uint32_t* mrow = masks + (int64_t)r * words;
@@ -259,7 +280,7 @@ __global__ __launch_bounds__(kSampT) void k_sip_count(const float* __restrict__ 
   int cnt = 0;
   for (int base = 0; base < 8 * words; base += kSampT) {
     const int g = base + t;
-    const uint32_t nib = g < groups ? draw_group(s, n, g, qb, h, b, seed, ps) : 0u;
+    const uint32_t nib = g < groups ? draw_group(s, n, g, qb, h, b, seed, ps, c32) : 0u;
     cnt += __popc(nib);
     // eight consecutive groups (threads) make one 32-bit mask word
     uint32_t wv = nib << (4 * (t & 7));
