@@ -139,6 +139,37 @@ def test_sampler_capacity_overflow_and_determinism():
     assert torch.equal(a.col_idx[:n], b.col_idx[:n]) and torch.equal(a.logw[:n], b.logw[:n])
 
 
+PLAN_PATHS = {
+    "bf16_ragged": (SEL["bf16_ragged"], 0.12),
+    "bf16_mid_half": (SEL["bf16_mid"], 0.5),
+    "bf16_mid_all": (SEL["bf16_mid"], 1.0),
+    "tiny_f32": (SEL["tiny_f32"], 0.3),
+    "bf16_d64_b2": (SEL["bf16_d64_b2"], 0.05),
+    # 38 000 key blocks: a row of 152 000 bytes, near the LDS limit of the count kernel
+    "bf16_long_row": (Workload("L", B=1, H=1, D=64, grid=(19, 40, 200)), 0.1),
+}
+
+
+@pytest.mark.parametrize("name", list(PLAN_PATHS))
+def test_plan_equals_scores_then_sampler(name):
+    # abatt_plan (scores in its workspace) and abatt_scores followed by
+    # abatt_plan_from_scores (scores in the caller's buffer) run the same
+    # kernels on the same scores: the same plan, bit for bit
+    wl, budget = PLAN_PATHS[name]
+    q, k, _ = make_qkv(wl)
+    prob = lib_problem(wl)
+    dq, dk = to_dev(q, wl.dtype), to_dev(k, wl.dtype)
+    say(f"plan paths {name} n_kbs={prob.n_kbs} budget {budget}")
+    a = ab.plan(dq, dk, budget, seed=4, problem=prob)
+    S, _, _ = ab.scores(dq, dk, prob)
+    b = ab.plan_from_scores(S, budget, 4, prob)
+    torch.cuda.synchronize()
+    assert a.ok() and b.ok()
+    assert torch.equal(a.row_ptr, b.row_ptr)
+    n = a.nnz()
+    assert torch.equal(a.col_idx[:n], b.col_idx[:n]) and torch.equal(a.logw[:n], b.logw[:n])
+
+
 @pytest.mark.parametrize("name", list(SEL))
 def test_plan_end_to_end_agreement(name):
     wl = SEL[name]
