@@ -29,9 +29,9 @@ ABATT_F32, ABATT_BF16 = 0, 1
 SYMBOLS = (
     "abatt_plan_rows", "abatt_plan_max_nnz", "abatt_plan_nnz_bound",
     "abatt_plan_workspace_bytes", "abatt_sampler_workspace_bytes", "abatt_plan",
-    "abatt_attend", "abatt_v_to_f16", "abatt_attend_v16", "abatt_dense", "abatt_key_means",
-    "abatt_scores",
-    "abatt_plan_from_scores", "abatt_status_str", "abatt_version",
+    "abatt_attend", "abatt_v_to_f16", "abatt_attend_v16", "abatt_dense",
+    "abatt_key_means", "abatt_scores", "abatt_plan_from_scores", "abatt_status_str",
+    "abatt_version",
 )
 
 
@@ -191,15 +191,40 @@ def _qkv_check(prob: Problem, *ts: torch.Tensor) -> None:
                              f"got {t.dtype} {tuple(t.shape)}")
 
 
-def _plan_check(prob: Problem, pl: Plan) -> None:
+def _plan_check(prob: Problem, pl: Plan, device=None, need_status: bool = False) -> None:
+    """Checks a plan's arrays against the problem before the library sees them:
+    the C ABI gets pointers and a capacity only, so a short or mistyped array
+    would be written or read out of bounds by the kernels."""
     if pl.row_ptr.numel() != prob.R + 1 or pl.row_ptr.dtype != torch.int32:
         raise ValueError(f"row_ptr must be int32 [{prob.R + 1}]")
     if pl.col_idx.dtype != torch.int32 or pl.logw.dtype != torch.float32 \
             or pl.logw.numel() < pl.col_idx.numel():
         raise ValueError("col_idx must be int32 and logw float32 of the same capacity")
-    for t in (pl.row_ptr, pl.col_idx, pl.logw):
+    arrays = [pl.row_ptr, pl.col_idx, pl.logw]
+    if need_status:
+        if pl.status is None:
+            raise ValueError("a plan written by plan() needs a status tensor")
+        if pl.status.dtype != torch.int32 or pl.status.numel() < 1:
+            raise ValueError("status must be an int32 tensor of at least one element")
+    if pl.status is not None:
+        arrays.append(pl.status)
+    for t in arrays:
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("plan arrays must be contiguous CUDA tensors")
+        if device is not None and t.device != device:
+            raise ValueError(f"plan arrays must be on {device}, found one on {t.device}")
+
+
+def _out_check(prob: Problem, out: torch.Tensor, like: torch.Tensor) -> None:
+    """A caller-supplied output must hold exactly [B,H,N,D] of the problem's
+    dtype, contiguous, on the inputs' device (the kernels write all of it)."""
+    if not isinstance(out, torch.Tensor) or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous CUDA tensor")
+    if out.device != like.device:
+        raise ValueError(f"out must be on {like.device}, found {out.device}")
+    if out.dtype != prob.torch_dtype or tuple(out.shape) != (prob.B, prob.H, prob.N, prob.D):
+        raise ValueError(f"out must be {prob.dtype} [{prob.B},{prob.H},{prob.N},{prob.D}], "
+                         f"got {out.dtype} {tuple(out.shape)}")
 
 
 def plan_rows(prob: Problem) -> int:
@@ -243,7 +268,13 @@ def plan(q: torch.Tensor, k: torch.Tensor, budget: float, seed: int = 0,
     if out is None:
         cap = nnz_bound(prob, budget) if capacity is None else capacity
         out = empty_plan(prob, cap, q.device)
-    ws = workspace(prob, q.device) if ws is None else ws
+    else:
+        _plan_check(prob, out, q.device, need_status=True)
+    if ws is None:
+        ws = workspace(prob, q.device)
+    elif not ws.is_cuda or not ws.is_contiguous() or ws.device != q.device \
+            or ws.dtype != torch.uint8:
+        raise ValueError(f"ws must be a contiguous uint8 tensor on {q.device}")
     cp = out.c()
     _check(lib.abatt_plan(ctypes.byref(prob.c()), _ptr(q), _ptr(k), float(budget),
                           ctypes.c_uint64(seed), _ptr(ws), ws.numel(), ctypes.byref(cp),
@@ -266,6 +297,8 @@ def v_to_f16(v: torch.Tensor, problem: Optional[Problem] = None,
     _qkv_check(prob, v)
     v16 = torch.empty(v.shape, dtype=torch.float16, device=v.device) if out is None else out
     _v16_check(prob, v16)
+    if v16.device != v.device:
+        raise ValueError(f"out must be on {v.device}, found {v16.device}")
     _check(load_library().abatt_v_to_f16(ctypes.byref(prob.c()), _ptr(v), _ptr(v16), _stream()))
     return v16
 
@@ -284,8 +317,15 @@ def attend(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pl: Plan,
         _v16_check(prob, v)
     else:
         _qkv_check(prob, v)
-    _plan_check(prob, pl)
-    o = torch.empty_like(q) if out is None else out
+    _plan_check(prob, pl, q.device)
+    for t in (k, v):
+        if t.device != q.device:
+            raise ValueError(f"q, k and v must be on one device ({q.device}, {t.device})")
+    if out is None:
+        o = torch.empty_like(q)
+    else:
+        _out_check(prob, out, q)
+        o = out
     lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32, device=q.device) \
         if return_lse else None
     cp = pl.c()
@@ -300,7 +340,14 @@ def dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, problem: Optional[P
     """Dense softmax attention over every key (abatt_dense)."""
     prob = problem or Problem.like(q)
     _qkv_check(prob, q, k, v)
-    o = torch.empty_like(q) if out is None else out
+    for t in (k, v):
+        if t.device != q.device:
+            raise ValueError(f"q, k and v must be on one device ({q.device}, {t.device})")
+    if out is None:
+        o = torch.empty_like(q)
+    else:
+        _out_check(prob, out, q)
+        o = out
     lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32, device=q.device) \
         if return_lse else None
     _check(load_library().abatt_dense(ctypes.byref(prob.c()), _ptr(q), _ptr(k), _ptr(v),

@@ -1,0 +1,83 @@
+"""The binding refuses caller buffers that do not fit the problem before
+anything is launched: the C ABI takes bare pointers (and a capacity), so a
+short, mistyped or misplaced output would otherwise be written out of bounds."""
+import pytest
+import torch
+
+from helpers import lib_problem, say, to_dev
+from workloads import Workload, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+ab = pytest.importorskip("block_sparse_attention_09_amd")
+
+WL = Workload("bind", B=1, H=2, D=128, grid=(2, 8, 16))
+
+
+@pytest.fixture(scope="module")
+def qkv():
+    q, k, v = make_qkv(WL)
+    return tuple(to_dev(x, WL.dtype) for x in (q, k, v))
+
+
+def test_plan_out_checked(qkv):
+    q, k, _ = qkv
+    prob = lib_problem(WL)
+    dev = q.device
+    say("binding: plan(out=...) checks")
+    good = ab.empty_plan(prob, ab.nnz_bound(prob, 0.1), dev)
+    other = ab.Problem(B=1, H=3, N=WL.N, D=128)          # another problem's plan
+    bad = {
+        "plan of another problem": ab.empty_plan(other, ab.nnz_bound(other, 0.1), dev),
+        "row_ptr int64": ab.Plan(good.row_ptr.long(), good.col_idx, good.logw, good.status),
+        "logw shorter than col_idx": ab.Plan(good.row_ptr, good.col_idx, good.logw[:-1], good.status),
+        "logw float64": ab.Plan(good.row_ptr, good.col_idx, good.logw.double(), good.status),
+        "no status": ab.Plan(good.row_ptr, good.col_idx, good.logw, None),
+        "status int64": ab.Plan(good.row_ptr, good.col_idx, good.logw, good.status.long()),
+        "row_ptr on the host": ab.Plan(good.row_ptr.cpu(), good.col_idx, good.logw, good.status),
+        "col_idx strided": ab.Plan(good.row_ptr, torch.empty(2 * good.col_idx.numel(),
+                                                             dtype=torch.int32, device=dev)[::2],
+                                   good.logw, good.status),
+    }
+    for what, pl in bad.items():
+        with pytest.raises(ValueError):
+            ab.plan(q, k, 0.1, seed=0, problem=prob, out=pl)
+    with pytest.raises(ValueError):
+        ab.plan(q, k, 0.1, seed=0, problem=prob, out=good,
+                ws=torch.empty(ab.plan_workspace_bytes(prob), dtype=torch.uint8))
+    # the good buffers are accepted
+    ab.plan(q, k, 0.1, seed=0, problem=prob, out=good)
+    torch.cuda.synchronize()
+    assert good.ok()
+
+
+def test_attend_and_dense_out_checked(qkv):
+    q, k, v = qkv
+    prob = lib_problem(WL)
+    say("binding: attend/dense(out=...) checks")
+    pl = ab.plan(q, k, 0.1, seed=0, problem=prob)
+    outs = {
+        "short": torch.empty(1, 2, WL.N - 4, 128, dtype=torch.bfloat16, device=q.device),
+        "float32": torch.empty(1, 2, WL.N, 128, dtype=torch.float32, device=q.device),
+        "transposed": torch.empty(1, 2, 128, WL.N, dtype=torch.bfloat16,
+                                  device=q.device).transpose(2, 3),
+        "host": torch.empty(1, 2, WL.N, 128, dtype=torch.bfloat16),
+    }
+    for what, o in outs.items():
+        with pytest.raises(ValueError):
+            ab.attend(q, k, v, pl, problem=prob, out=o)
+        with pytest.raises(ValueError):
+            ab.dense(q, k, v, problem=prob, out=o)
+    v16 = ab.v_to_f16(v, prob)
+    with pytest.raises(ValueError):
+        ab.attend(q, k, v16, pl, problem=prob, out=outs["short"])
+    with pytest.raises(ValueError):
+        ab.v_to_f16(v, prob, out=torch.empty(1, 2, WL.N, 128, dtype=torch.bfloat16,
+                                              device=q.device))
+    # the right buffer is written
+    o = torch.full_like(q, float("nan"))
+    ab.attend(q, k, v, pl, problem=prob, out=o)
+    o2 = torch.full_like(q, float("nan"))
+    ab.dense(q, k, v, problem=prob, out=o2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(o2.float()).all()
