@@ -25,11 +25,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libabatt.so")
 
 ABATT_F32, ABATT_BF16 = 0, 1
+ABATT_ESCRATCH = -6
+SCRATCH_BYTES = 256 * 1024 * 1024   # ABATT_SCRATCH_BYTES in abatt.h
 
 SYMBOLS = (
     "abatt_plan_rows", "abatt_plan_max_nnz", "abatt_plan_nnz_bound",
     "abatt_plan_workspace_bytes", "abatt_sampler_workspace_bytes", "abatt_plan",
-    "abatt_attend", "abatt_v_to_f16", "abatt_attend_v16", "abatt_dense",
+    "abatt_plan_noalloc", "abatt_attend", "abatt_v_to_f16", "abatt_attend_v16", "abatt_dense",
     "abatt_key_means", "abatt_scores", "abatt_plan_from_scores", "abatt_status_str",
     "abatt_version",
 )
@@ -71,6 +73,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "abatt_sampler_workspace_bytes": (sz, [P]),
         "abatt_plan": (st, [P, vp, vp, ctypes.c_double, ctypes.c_uint64, vp, sz,
                             ctypes.POINTER(_Plan), vp]),
+        "abatt_plan_noalloc": (st, [P, vp, vp, ctypes.c_double, ctypes.c_uint64,
+                                    ctypes.POINTER(_Plan), vp]),
         "abatt_attend": (st, [P, vp, vp, vp, ctypes.POINTER(_Plan), vp, vp, vp]),
         "abatt_v_to_f16": (st, [P, vp, vp, vp]),
         "abatt_attend_v16": (st, [P, vp, vp, vp, ctypes.POINTER(_Plan), vp, vp, vp]),
@@ -279,6 +283,25 @@ def plan(q: torch.Tensor, k: torch.Tensor, budget: float, seed: int = 0,
     _check(lib.abatt_plan(ctypes.byref(prob.c()), _ptr(q), _ptr(k), float(budget),
                           ctypes.c_uint64(seed), _ptr(ws), ws.numel(), ctypes.byref(cp),
                           _stream()))
+    return out
+
+
+def plan_noalloc(q: torch.Tensor, k: torch.Tensor, budget: float, seed: int = 0,
+                 problem: Optional[Problem] = None, out: Optional[Plan] = None,
+                 capacity: Optional[int] = None) -> Plan:
+    """abatt_plan_noalloc: the same plan as plan(), with the library's static
+    scratch as workspace.  Pass `out` (from empty_plan) to allocate nothing."""
+    prob = problem or Problem.like(q)
+    _qkv_check(prob, q, k)
+    if out is None:
+        cap = nnz_bound(prob, budget) if capacity is None else capacity
+        out = empty_plan(prob, cap, q.device)
+    else:
+        _plan_check(prob, out, q.device, need_status=True)
+    cp = out.c()
+    _check(load_library().abatt_plan_noalloc(ctypes.byref(prob.c()), _ptr(q), _ptr(k),
+                                             float(budget), ctypes.c_uint64(seed),
+                                             ctypes.byref(cp), _stream()))
     return out
 
 

@@ -124,6 +124,19 @@ hipError_t run_scores(const Shape& s, const PlanWs& l, char* ws, const void* Q, 
   return e;
 }
 
+// The whole plan (selector, then sampler) on the workspace `ws` laid out as l.
+hipError_t run_plan(const Shape& s, const PlanWs& l, char* ws, const void* Q, const void* K,
+                    double budget, uint64_t seed, const abatt_plan_t* plan, hipStream_t stream) {
+  float* mu = reinterpret_cast<float*>(ws + l.mu);
+  float* w = reinterpret_cast<float*>(ws + l.w);
+  float* S = reinterpret_cast<float*>(ws + l.S);
+  hipError_t e = run_scores(s, l, ws, Q, K, mu, w, S, stream);
+  if (e == hipSuccess)
+    e = abatt::launch_sampler(s, S, budget, seed, ws + l.sampler, plan->row_ptr, plan->col_idx,
+                              plan->logw, plan->capacity, plan->status, stream);
+  return e;
+}
+
 bool budget_ok(double budget) { return budget > 0.0 && budget <= 1.0 && std::isfinite(budget); }
 
 abatt_status check_plan(const Shape& s, const abatt_plan_t* plan, bool need_status) {
@@ -224,15 +237,26 @@ abatt_status abatt_plan(const abatt_problem_t* p, const void* Q, const void* K, 
   const PlanWs l = plan_ws_layout(s);
   if (workspace_bytes < l.total) return ABATT_EWORKSPACE;
   if (plan->capacity < (int64_t)s.R * (s.n_kb - s.n_kbs)) return ABATT_ECAPACITY;
-  char* ws = static_cast<char*>(workspace);
-  float* mu = reinterpret_cast<float*>(ws + l.mu);
-  float* w = reinterpret_cast<float*>(ws + l.w);
-  float* S = reinterpret_cast<float*>(ws + l.S);
-  hipError_t e = run_scores(s, l, ws, Q, K, mu, w, S, stream);
-  if (e == hipSuccess)
-    e = abatt::launch_sampler(s, S, budget, seed, ws + l.sampler, plan->row_ptr, plan->col_idx,
-                              plan->logw, plan->capacity, plan->status, stream);
-  return hip_status(e);
+  return hip_status(run_plan(s, l, static_cast<char*>(workspace), Q, K, budget, seed, plan,
+                             stream));
+}
+
+abatt_status abatt_plan_noalloc(const abatt_problem_t* p, const void* Q, const void* K,
+                                double budget, uint64_t seed, abatt_plan_t* plan,
+                                hipStream_t stream) {
+  Shape s;
+  abatt_status st = make_shape(p, &s);
+  if (st != ABATT_OK) return st;
+  if (bad(Q) || bad(K) || !budget_ok(budget)) return ABATT_EINVAL;
+  st = check_plan(s, plan, true);
+  if (st != ABATT_OK) return st;
+  const PlanWs l = plan_ws_layout(s);
+  if (l.total > (size_t)ABATT_SCRATCH_BYTES) return ABATT_ESCRATCH;
+  if (plan->capacity < (int64_t)s.R * (s.n_kb - s.n_kbs)) return ABATT_ECAPACITY;
+  void* ws = nullptr;
+  hipError_t e = abatt::scratch_ptr(&ws);
+  if (e != hipSuccess) return ABATT_EHIP;
+  return hip_status(run_plan(s, l, static_cast<char*>(ws), Q, K, budget, seed, plan, stream));
 }
 
 abatt_status abatt_attend(const abatt_problem_t* p, const void* Q, const void* K, const void* V,
@@ -291,6 +315,7 @@ const char* abatt_status_str(abatt_status s) {
     case ABATT_EWORKSPACE: return "workspace too small";
     case ABATT_ECAPACITY: return "plan capacity too small";
     case ABATT_EHIP: return "HIP launch failed";
+    case ABATT_ESCRATCH: return "plan workspace exceeds the library's static scratch (ABATT_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

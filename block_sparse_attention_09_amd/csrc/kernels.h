@@ -55,4 +55,8 @@ hipError_t launch_attend(const Shape& s, const void* Q, const void* K, const voi
 // attend.hip: V [B,H,N,D] bf16 -> fp16 (round toward zero)
 hipError_t launch_v_to_f16(const Shape& s, const void* V, void* V16, hipStream_t st);
 
+// scratch.hip: device address of the library's static scratch array
+// (ABATT_SCRATCH_BYTES) on the current device, looked up on first use
+hipError_t scratch_ptr(void** out);
+
 }  // namespace abatt

@@ -8,8 +8,10 @@
  *   abatt_dense   Q, K, V         -> O (+ log-sum-exp), every key, no shift
  *
  * abatt_v_to_f16 + abatt_attend_v16 split abatt_attend in two (V converted to
- * fp16 once per call; the same results from a faster kernel), plus test hooks that enter the same kernels part-way (abatt_key_means,
- * abatt_scores, abatt_plan_from_scores).
+ * fp16 once per call; the same results from a faster kernel);
+ * abatt_plan_noalloc is abatt_plan without a caller workspace; test hooks
+ * enter the same kernels part-way (abatt_key_means, abatt_scores,
+ * abatt_plan_from_scores).
  *
  * Pages this follows:
  *   [hamidun]  news.hamidun.com, "AB-Attention speeds up video generation by
@@ -35,7 +37,9 @@
  *     are written to plan->status without a sync.  Faults inside kernels
  *     surface at the caller's next synchronisation.
  *   - The library holds no state between calls and is thread-safe.  Calls on
- *     different streams need their own workspaces and plans.
+ *     different streams need their own workspaces and plans.  The one
+ *     exception is abatt_plan_noalloc, whose workspace is a static device
+ *     array of the library shared by every call on a GPU (see there).
  *   - Query block qb holds tokens [q_block*qb, min(q_block*(qb+1), N)); key
  *     block j holds tokens [kv_block*j, kv_block*j + kv_block).  The last
  *     n_forced_tail tokens (text tokens) form "forced" key blocks that are not
@@ -60,8 +64,15 @@ typedef enum {
   ABATT_EUNSUPPORTED = -2,  /* valid, but outside what the kernels implement */
   ABATT_EWORKSPACE = -3,    /* workspace smaller than *_workspace_bytes()     */
   ABATT_ECAPACITY = -4,     /* plan capacity below what the call may need     */
-  ABATT_EHIP = -5           /* a HIP launch failed                            */
+  ABATT_EHIP = -5,          /* a HIP launch failed                            */
+  ABATT_ESCRATCH = -6       /* problem needs more than ABATT_SCRATCH_BYTES of */
+                            /* plan workspace (abatt_plan_noalloc)            */
 } abatt_status;
+
+/* Size of the library's own device scratch array, which abatt_plan_noalloc
+   uses as its plan workspace (256 MiB: the plan workspace of up to the
+   12-head, 32760-token 480p layer, about 167 MB). */
+#define ABATT_SCRATCH_BYTES (256u * 1024u * 1024u)
 
 typedef enum { ABATT_F32 = 0, ABATT_BF16 = 1 } abatt_dtype;
 
@@ -142,6 +153,31 @@ abatt_status abatt_plan(const abatt_problem_t *p, const void *Q, const void *K,
                         double budget, uint64_t seed, void *workspace,
                         size_t workspace_bytes, abatt_plan_t *plan,
                         hipStream_t stream);
+
+/*
+ * abatt_plan_noalloc -- abatt_plan for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, checks and results (bit for bit) as
+ * abatt_plan, without the workspace: the plan workspace lives in a static
+ * device array of ABATT_SCRATCH_BYTES inside the library, one per GPU,
+ * held from the library's first use on that GPU until the process ends.
+ * The call itself allocates and frees nothing; the caller still provides Q,
+ * K and the plan buffers.
+ *   - Returns ABATT_ESCRATCH, before any HIP call, when
+ *     abatt_plan_workspace_bytes(p) > ABATT_SCRATCH_BYTES (call it per group
+ *     of heads instead: the plan rows of a head depend on that head only).
+ *   - Every call on one GPU shares that GPU's array, and the array keeps the
+ *     last call's contents (every kernel writes its part before reading it,
+ *     so nothing has to be cleared).  Calls that overlap on one GPU -- on
+ *     different streams, or from different threads without ordering -- race
+ *     on the array and give undefined plans: serialise them.
+ *   - The device address of the array is looked up on the first call on
+ *     each device (hipGetSymbolAddress, with that device current);
+ *     ABATT_EHIP if that fails.
+ */
+abatt_status abatt_plan_noalloc(const abatt_problem_t *p, const void *Q, const void *K,
+                                double budget, uint64_t seed, abatt_plan_t *plan,
+                                hipStream_t stream);
 
 /*
  * abatt_attend -- softmax attention over the plan's gathered key blocks.

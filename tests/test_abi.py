@@ -137,8 +137,38 @@ def test_argument_checks_before_any_hip_call(lib):
     assert lib.abatt_dense(P(prob(N=1023, D=96).c()), fake, fake, fake, fake, None, None) == -2
 
 
+def test_noalloc_checks_before_any_hip_call(lib):
+    """abatt_plan_noalloc refuses a problem whose plan workspace exceeds the
+    static scratch (ABATT_ESCRATCH), and bad arguments, with nothing enqueued."""
+    P = ctypes.byref
+    fake = ctypes.c_void_p(0x1000)
+    good = ab._Plan(0x1000, 0x1000, 0x1000, 10 ** 9, 0x1000)
+    big = ab.Problem(B=1, H=40, N=75600, D=128)          # 14B 720p layer: ~2.3 GB
+    assert ab.plan_workspace_bytes(big) > ab.SCRATCH_BYTES
+    assert lib.abatt_plan_noalloc(P(big.c()), fake, fake, 0.1, 0, P(good), None) == -6
+    fits = ab.Problem(B=1, H=12, N=32760, D=128)          # 1.3B 480p layer fits
+    assert ab.plan_workspace_bytes(fits) <= ab.SCRATCH_BYTES
+    c = prob().c()
+    assert lib.abatt_plan_noalloc(P(c), None, fake, 0.1, 0, P(good), None) == -1
+    assert lib.abatt_plan_noalloc(P(c), fake, ctypes.c_void_p(0x1008), 0.1, 0, P(good), None) == -1
+    assert lib.abatt_plan_noalloc(P(c), fake, fake, 0.0, 0, P(good), None) == -1
+    nostat = ab._Plan(0x1000, 0x1000, 0x1000, 10 ** 6, None)
+    assert lib.abatt_plan_noalloc(P(c), fake, fake, 0.1, 0, P(nostat), None) == -1
+    pf = prob(N=1280, n_forced_tail=256).c()
+    small = ab._Plan(0x1000, 0x1000, 0x1000, 10, 0x1000)
+    assert lib.abatt_plan_noalloc(P(pf), fake, fake, 0.1, 0, P(small), None) == -4
+    assert lib.abatt_plan_noalloc(P(prob(D=96).c()), fake, fake, 0.1, 0, P(good), None) == -2
+
+
+def test_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "abatt.h")).read()
+    m = re.search(r"#define ABATT_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", text)
+    assert m is not None
+    assert int(m.group(1)) * 1024 * 1024 == ab.SCRATCH_BYTES
+
+
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert len(lib.abatt_status_str(code)) > 0
     with pytest.raises(ab.AbattError):
         ab._check(-1)

@@ -45,6 +45,8 @@ def test_plan_out_checked(qkv):
     with pytest.raises(ValueError):
         ab.plan(q, k, 0.1, seed=0, problem=prob, out=good,
                 ws=torch.empty(ab.plan_workspace_bytes(prob), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        ab.plan_noalloc(q, k, 0.1, seed=0, problem=prob, out=bad["plan of another problem"])
     # the good buffers are accepted
     ab.plan(q, k, 0.1, seed=0, problem=prob, out=good)
     torch.cuda.synchronize()
