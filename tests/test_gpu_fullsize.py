@@ -7,8 +7,10 @@ sample of rows one by one:
     bar: max-abs 1e-2, mean-rel 1e-3 against the oracle rounded to bf16), and
     the fp16-V form (V converted once, as bench.py runs it) bit-identical to it;
   * dense rows against the oracle's dense attention of sampled queries.
-Sampled rows lie in the first two heads (the oracle gets those heads' inputs,
-generated on the host by the same seeded recipe).
+Sampled rows lie in the first two heads and the last head (its first row, a
+middle row and its last row, the head's partial last query block); the oracle
+gets those heads' inputs, generated on the host by the same seeded recipe
+(full-shape host arrays whose other heads stay zero and untouched).
 """
 import numpy as np
 import pytest
@@ -23,8 +25,15 @@ pytestmark = pytest.mark.gpu
 ab = pytest.importorskip("block_sparse_attention_09_amd")
 
 
+def checked_heads(wl):
+    return sorted({0, min(1, wl.H - 1), wl.H - 1})
+
+
 def gpu_inputs(wl):
-    """Full [B,H,N,D] bf16 q, k, v on the GPU, plus host fp32 masters of q, k."""
+    """Full [B,H,N,D] bf16 q, k, v on the GPU; host fp32 masters of q, k (reused
+    plans); and host q, k, v rounded like the GPU's for the checked heads of
+    batch 0, in full-shape arrays whose other heads are zero (np.zeros pages
+    that are never written take no memory)."""
     shape = (wl.B, wl.H, wl.N, wl.D)
     q = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
     k = torch.empty_like(q)
@@ -32,13 +41,18 @@ def gpu_inputs(wl):
     gen = Generator(wl)
     qm = np.empty(shape, dtype=np.float32) if wl.plan_reuse > 1 else None
     km = np.empty(shape, dtype=np.float32) if wl.plan_reuse > 1 else None
+    host = tuple(np.zeros(shape, dtype=np.float32) for _ in range(3))
+    heads = checked_heads(wl)
     for b, h, qh, kh, vh in gen.iter_heads():
         q[b, h].copy_(torch.from_numpy(qh).to(torch.bfloat16))
         k[b, h].copy_(torch.from_numpy(kh).to(torch.bfloat16))
         v[b, h].copy_(torch.from_numpy(vh).to(torch.bfloat16))
         if qm is not None:
             qm[b, h], km[b, h] = qh, kh
-    return gen, q, k, v, qm, km
+        if b == 0 and h in heads:
+            for arr, x in zip(host, (qh, kh, vh)):
+                arr[0, h] = round_like(x, wl.dtype)
+    return gen, q, k, v, qm, km, host
 
 
 def problems(wl):
@@ -50,15 +64,21 @@ def problems(wl):
 
 
 def sample_rows(op, n=6, seed=0):
+    """Rows of heads 0 and 1 (random ones and the partial last blocks) and of
+    the last head: its first, a middle and its last row (R - 1)."""
     rng = np.random.default_rng(seed)
     last = op.n_qb - 1
     rows = {0, last, op.n_qb + last // 2, op.n_qb + last}      # incl. partial last blocks
     rows |= set(rng.integers(0, 2 * op.n_qb, n).tolist())
-    return sorted(r for r in rows if r < min(2, op.H) * op.n_qb)
+    rows = {r for r in rows if r < min(2, op.H) * op.n_qb}
+    hl = (op.B * op.H - 1) * op.n_qb                            # last head of the last batch
+    if op.B == 1:
+        rows |= {hl, hl + last // 2, op.R - 1}
+    return sorted(rows)
 
 
 def check_plan_and_attend(tag, wl, budget, seed, q2, k2, v2, q, k, v, prob, op, pl, o):
-    """q2/k2/v2: host fp32 (bf16-exact) inputs of heads 0..1; q/k/v, pl, o: GPU."""
+    """q2/k2/v2: host fp32 (bf16-exact) inputs of the checked heads; q/k/v, pl, o: GPU."""
     rows = sample_rows(op)
     ref = oracle.plan(q2, k2, op, budget, seed, rows=rows)
     rp = pl.row_ptr.cpu().numpy().astype(np.int64)
@@ -93,9 +113,8 @@ def check_rows(tag, q2, k2, v2, op, rows, cols, lws, o):
 def test_fullsize_plan_attend(name):
     wl = CONFIGS[name]
     say(f"{name}: generating inputs")
-    gen, q, k, v, _, _ = gpu_inputs(wl)
+    gen, q, k, v, _, _, (q2, k2, v2) = gpu_inputs(wl)
     prob, op = problems(wl)
-    q2, k2, v2 = make_qkv(wl, heads=2)
     # every sparse budget the layer is quoted at (8%, 10%, 12% for the 14B layer)
     for budget in [b for b in wl.budgets if b < 1.0]:
         pl = ab.plan(q, k, budget, seed=wl.plan_seed, problem=prob)
@@ -119,7 +138,7 @@ def test_fullsize_plan_attend(name):
         torch.cuda.synchronize()
         rng = np.random.default_rng(1)
         qi = np.unique(np.concatenate([[0, wl.N - 1], rng.integers(0, wl.N, 30)]))
-        for h in (0, 1):
+        for h in checked_heads(wl):
             Od, _ = oracle.dense_rows(q2, k2, v2, op, 0, h, qi)
             got = od[0, h, qi].float().cpu().numpy().astype(np.float64)
             mx, mr = errors(got, round_ref(Od, "bf16"))
@@ -132,13 +151,13 @@ def test_fullsize_stress_plan_reuse():
     wl = CONFIGS["stress_1pct"]
     budget = wl.budgets[0]
     say("stress_1pct: generating inputs")
-    gen, q, k, v, qm, km = gpu_inputs(wl)
+    gen, q, k, v, qm, km, (q2, k2, v2) = gpu_inputs(wl)
     prob, op = problems(wl)
     pl = ab.plan(q, k, budget, seed=wl.plan_seed, problem=prob)
     torch.cuda.synchronize()
     assert pl.ok()
     seq = make_qkv_sequence(wl, wl.plan_reuse, heads=2)
-    q2, k2, v2 = seq[0]
+    np.testing.assert_array_equal(q2[0, :2], seq[0][0][0])
     o = ab.attend(q, k, v, pl, problem=prob)
     torch.cuda.synchronize()
     check_plan_and_attend("stress call 0", wl, budget, wl.plan_seed, q2, k2, v2, q, k, v,
@@ -154,8 +173,14 @@ def test_fullsize_stress_plan_reuse():
                 k[b, h].copy_(torch.from_numpy(km[b, h]).to(torch.bfloat16))
         o = ab.attend(q, k, v, pl, problem=prob)
     torch.cuda.synchronize()
-    q3, k3, v3 = seq[-1]
-    np.testing.assert_array_equal(q[0, :2].float().cpu().numpy(), q3[0])
+    np.testing.assert_array_equal(q[0, :2].float().cpu().numpy(), seq[-1][0][0])
+    # host inputs of the last call for the checked heads (the drifted masters)
+    q3, k3 = np.zeros_like(q2), np.zeros_like(k2)
+    for h in checked_heads(wl):
+        q3[0, h] = round_like(qm[0, h], wl.dtype)
+        k3[0, h] = round_like(km[0, h], wl.dtype)
+    np.testing.assert_array_equal(q3[0, :2], seq[-1][0][0])
+    v3 = v2
     rows = sample_rows(op)
     rp = pl.row_ptr.cpu().numpy().astype(np.int64)
     ci = pl.col_idx[: int(rp[-1])].cpu().numpy()
@@ -171,9 +196,8 @@ def test_sharp_inputs_plan_attend(pe_amp):
     still has to agree with the oracle's (>= 99%) and attention to hold its bar."""
     wl = CONFIGS["wan1p3b_480p"].scaled(H=2, pe_amp=pe_amp)
     say(f"wan1p3b_480p H=2 pe_amp={pe_amp}: generating inputs")
-    gen, q, k, v, _, _ = gpu_inputs(wl)
+    gen, q, k, v, _, _, (q2, k2, v2) = gpu_inputs(wl)
     prob, op = problems(wl)
-    q2, k2, v2 = make_qkv(wl, heads=2)
     budget = 0.10
     pl = ab.plan(q, k, budget, seed=wl.plan_seed, problem=prob)
     o = ab.attend(q, k, v, pl, problem=prob)

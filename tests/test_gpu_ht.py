@@ -8,7 +8,8 @@ softmax normalisation without bias (the normalised output itself is not
 unbiased, and nothing here assumes it is).
 
 Over many seeds, with the plan and the attention both run by the library on
-the GPU (fp32 path, tiny workload):
+the GPU -- the fp32 path (D = 64) and the bf16 production path (D = 128: fp16
+block scores, fp16 probabilities times fp16 V, bf16 output):
   * each block's inclusion frequency matches pi = exp(-logw) of the plan (the
     scores do not depend on the seed, so every kept copy of a block carries
     the same logw) -- a z-test per block;
@@ -31,12 +32,20 @@ pytestmark = pytest.mark.gpu
 ab = pytest.importorskip("block_sparse_attention_09_amd")
 
 
-def test_sip_law_and_ht_unbiasedness_on_gpu():
-    wl = Workload("ht", B=1, H=1, D=64, grid=(1, 16, 16), dtype="f32", sigma=1.0)
+HT_CASES = {
+    "f32_d64": Workload("ht", B=1, H=1, D=64, grid=(1, 16, 16), dtype="f32", sigma=1.0),
+    "bf16_d128": Workload("ht16", B=1, H=1, D=128, grid=(1, 16, 16), dtype="bf16", sigma=1.0),
+}
+
+
+@pytest.mark.parametrize("case", list(HT_CASES))
+def test_sip_law_and_ht_unbiasedness_on_gpu(case):
+    wl = HT_CASES[case]
     q, k, v = make_qkv(wl)
     op = oracle_problem(wl)
     prob = lib_problem(wl)
-    dq, dk, dv = (to_dev(x, "f32") for x in (q, k, v))
+    dq, dk, dv = (to_dev(x, wl.dtype) for x in (q, k, v))
+    say(f"HT law on GPU: {case}")
     Od, Ld = oracle.dense(q, k, v, op)
     budget, T = 0.1, 3000
     n, R, nq = op.n_kbs, op.R, 128
@@ -54,7 +63,7 @@ def test_sip_law_and_ht_unbiasedness_on_gpu():
         nnz = int(rp[-1])
         ci = pl.col_idx[:nnz].cpu().numpy()
         lw = pl.logw[:nnz].cpu().numpy()
-        o, lse = o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+        o, lse = o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
         for r in range(R):
             c, w = ci[rp[r]:rp[r + 1]], lw[rp[r]:rp[r + 1]]
             hits[r, c] += 1

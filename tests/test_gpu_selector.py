@@ -9,6 +9,8 @@
   1 fp32 ulp (float64 log on both sides, rounded to fp32);
 * abatt_plan end to end: >= 99% block agreement (Jaccard over all rows).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -41,6 +43,44 @@ def test_key_means(name):
     got = ab.key_means(to_dev(k, wl.dtype), lib_problem(wl))
     torch.cuda.synchronize()
     np.testing.assert_allclose(got.cpu().numpy(), ref, rtol=2e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("name", [n for n in SEL if SEL[n].dtype == "bf16"])
+def test_key_means_scoring_form(name):
+    """The key means as abatt_plan's scorer reads them (bf16 problems): one fp16
+    plane [B,H,n_kbs,D] at the start of the plan workspace, followed by one fp32
+    scale 2^e per tile of 32 blocks of a head.  plane * scale must be the mean
+    to fp16's rounding: 2^-11 relative, plus half an fp16 subnormal step (2^-25
+    in plane units) for values 2^-28 below their tile's largest."""
+    wl = SEL[name]
+    q, k, v = make_qkv(wl)
+    op = oracle_problem(wl)
+    prob = lib_problem(wl)
+    ref = oracle.key_block_means(k, op)                       # [B,H,n_kbs,D] float64
+    dq, dk = to_dev(q, wl.dtype), to_dev(k, wl.dtype)
+    ws = ab.workspace(prob, dq.device)
+    S = torch.empty(prob.R, prob.n_kbs, dtype=torch.float32, device="cuda")
+    say(f"key means scoring form {name}")
+    lib = ab.load_library()
+    ab._check(lib.abatt_scores(ctypes.byref(prob.c()), ab._ptr(dq), ab._ptr(dk), ab._ptr(S),
+                               None, None, ab._ptr(ws), ws.numel(), ab._stream()))
+    torch.cuda.synchronize()
+    n_plane = prob.B * prob.H * prob.n_kbs * prob.D
+    n_tiles = (prob.n_kbs + 31) // 32
+    raw = ws.cpu().numpy()
+    plane = raw[:2 * n_plane].view(np.float16).astype(np.float64)
+    plane = plane.reshape(prob.B, prob.H, prob.n_kbs, prob.D)
+    scale = raw[2 * n_plane:2 * n_plane + 4 * prob.B * prob.H * n_tiles].view(np.float32)
+    scale = scale.astype(np.float64).reshape(prob.B, prob.H, n_tiles)
+    # scales are powers of two that put each tile's largest |mean| in [2^14, 2^15)
+    assert np.all(np.log2(scale) == np.round(np.log2(scale)))
+    tile = np.repeat(scale, 32, axis=2)[:, :, :prob.n_kbs, None]
+    got = plane * tile
+    err = np.abs(got - ref)
+    bound = 2.0 ** -11 * np.abs(ref) + 2.0 ** -25 * tile + 1e-30
+    say(f"  max error / bound {np.max(err / bound):.3f}, max rel {np.max(err / np.maximum(np.abs(ref), 1e-30)):.2e}")
+    assert np.all(err <= bound)
+    assert np.abs(plane).max() < 2.0 ** 15
 
 
 @pytest.mark.parametrize("name", list(SEL))
