@@ -74,6 +74,7 @@ def cpu_baseline(wl: Workload, budget: float, dense_flop_per_head: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    host_cores = len(os.sched_getaffinity(0))
     from workloads import make_qkv
     q, k, v = make_qkv(wl, heads=1)
     op = oracle.Problem(B=1, H=1, N=wl.N, D=wl.D, kv_block=wl.kv_block, n_clusters=wl.n_clusters,
@@ -85,14 +86,20 @@ def cpu_baseline(wl: Workload, budget: float, dense_flop_per_head: float):
     oracle.attend(q, k, v, pl, op, rows=rows)
     t2 = time.perf_counter()
     sec = t2 - t0
+    # the oracle's matrix products run on the BLAS threads; the rest of it is
+    # single-threaded NumPy, so the BLAS thread count is what it used
     return {
         "value": dense_flop_per_head / sec / 1e12,
         "unit": "TFLOP/s (dense-equivalent)",
         "cores": int(threads),
+        "blas_threads": int(threads),
+        "host_cores": int(host_cores),
         "kind": "oracle",
-        "sample": f"1 of {wl.H} heads ({op.R} plan rows) of {wl.name}: oracle.plan + "
+        "sample": f"1 of {wl.H * wl.B} heads ({op.R} plan rows) of {wl.name}: oracle.plan + "
                   f"oracle.attend at budget {budget}; plan {t1 - t0:.1f} s, attend "
-                  f"{t2 - t1:.1f} s (per-head rate; heads are independent)",
+                  f"{t2 - t1:.1f} s; value is that head's rate, extrapolated to the layer "
+                  f"(heads are independent units of the same work)",
+        "extrapolated": True,
         "ms_per_call_extrapolated": sec * wl.H * wl.B * 1e3,
     }
 

@@ -2,10 +2,10 @@
 //
 // [hamidun] = news.hamidun.com, "AB-Attention speeds up video generation by up
 // to 2.23x and skips 92% of attention", section "AB-Attention's three
-// techniques", SIP paragraph: each key block is sampled with probability
-// proportional to its score, the most important blocks are certain, and a
-// kept block is weighted by the inverse of its probability (Horvitz-Thompson),
-// applied as the logit shift log(1/pi).
+// techniques", SIP paragraph: the draw probability pi of a key block scales
+// with its score and is capped at 1 (top-scored blocks always drawn); a drawn
+// block carries the Horvitz-Thompson weight 1/pi, applied as the logit shift
+// log(1/pi).
 //
 // Per plan row (one work-group, the score row staged in LDS):
 //   * pi: m = budget * n expected blocks; repeat c = (m - #certain) /
@@ -27,6 +27,7 @@
 // the recorded solve.  Forced (text) blocks follow the sampled ones with
 // logw 0.
 #include "common.h"
+#include "draw_rule.h"
 #include "kernels.h"
 
 namespace abatt {
@@ -227,11 +228,8 @@ __device__ __forceinline__ double pi_x32(float s, const PiSolve& ps, double c32)
 
 // Kept-bit mask (4 bits) of blocks 4g..4g+3: two Philox calls (counters 2g
 // and 2g+1), each giving two 53-bit uniforms u = w0 * 2^21 + (w1 >> 11)
-// (words 0,1 and 2,3); kept iff u < pi * 2^53.  With x = pi * 2^32 and
-// f = floor(min(x, 2^32 - 1)), w0 < f implies u < (w0 + 1) * 2^21 <= pi * 2^53
-// and w0 > f implies u >= (f + 1) * 2^21 > pi * 2^53 (for pi < 1; pi = 1
-// gives f = 2^32 - 1 and no w0 above it), so only w0 == f (probability 2^-32)
-// needs the 53-bit compare.
+// (words 0,1 and 2,3); kept iff u < pi * 2^53, decided by sip_keep
+// (draw_rule.h) on the first word except on a tie.
 __device__ __forceinline__ uint32_t draw_group(const float* s, int n, int g, int qb, int h, int b,
                                                uint64_t seed, const PiSolve& ps, double c32) {
   uint32_t mask = 0;
@@ -243,15 +241,7 @@ __device__ __forceinline__ uint32_t draw_group(const float* s, int n, int g, int
     for (int k = 0; k < 2; ++k) {
       const int j = 4 * g + 2 * i + k;
       if (j < n) {
-        const double x = pi_x32(s[j], ps, c32);
-        const uint32_t w0 = c[2 * k];
-        const uint32_t f = x < 4294967295.0 ? (uint32_t)x : 0xffffffffu;
-        bool keep = w0 < f;
-        if (w0 == f) {
-          const double u = (double)(((uint64_t)w0 << 21) | (c[2 * k + 1] >> 11));
-          keep = u < x * 2097152.0;
-        }
-        if (keep) mask |= 1u << (2 * i + k);
+        if (sip_keep(c[2 * k], c[2 * k + 1], pi_x32(s[j], ps, c32))) mask |= 1u << (2 * i + k);
       }
     }
   }

@@ -2,8 +2,8 @@
 //
 // [hamidun] = news.hamidun.com, "AB-Attention speeds up video generation by up
 // to 2.23x and skips 92% of attention", section "AB-Attention's three
-// techniques", IBCS paragraph: a key block's score is the weighted attention
-// of the block's centroids to its averaged keys.
+// techniques", IBCS paragraph: per-centroid softmax over the key-block means,
+// summed with the cluster shares as weights,
 //   s_j = sum_c w_c * softmax_j(scale * mu_c . kmean_j),   j over sparse blocks.
 //
 // One work-group holds 256 centroid rows (256/C query blocks of one head) and

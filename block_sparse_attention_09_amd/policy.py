@@ -7,7 +7,7 @@ Source: news.hamidun.com, "AB-Attention speeds up video generation by up to
     once every four denoising steps while the attention itself runs at every
     step;
   * section "How it was measured and what came out": in the evaluation the
-    first transformer block and the first 10 of 50 steps use full attention
+    opening transformer block (all steps) and steps 0-9 of the 50 run dense
     (for every method compared).
 Readings where the pages are silent:
   * a plan belongs to one transformer block (each block has its own q/k);
@@ -92,7 +92,12 @@ class ABAttention:
     denoising step s.  Each call runs the library's dense kernel, builds a new
     plan (abatt_plan) and attends with it, or attends with the block's cached
     plan (abatt_attend), as the policy says.  Plans stay on the device between
-    steps; a plan that outgrew its capacity raises.  For bf16 inputs the sparse
+    steps.  A plan that outgrew its capacity raises, without stalling the
+    host at every build: its status is copied to pinned host memory behind an
+    event, and checked at the next call once that event has completed (and at
+    the block's next build, or by ``check()``, which waits).  An overflowed
+    plan makes attention return zeros for the calls made before the error
+    surfaces.  For bf16 inputs the sparse
     calls convert V to fp16 once per call and use the attention's fp16-V form
     (abatt_v_to_f16 + abatt_attend_v16: the same results, a faster kernel)
     unless ``fp16_v`` is False.
@@ -110,10 +115,31 @@ class ABAttention:
         self.step = 0
         self._plans: Dict[int, Tuple[int, Plan, Problem]] = {}
         self._v16: Optional[torch.Tensor] = None   # reused fp16 copy of V
+        # plan status checks in flight: block -> (event, pinned int32 [1], step)
+        self._pending: Dict[int, Tuple[torch.cuda.Event, torch.Tensor, int]] = {}
+        self._status_host: Dict[int, torch.Tensor] = {}
         self.log: list = []    # (step, block, mode) of every call
 
     def set_step(self, step: int) -> None:
         self.step = step
+
+    def _check_block(self, block: int, wait: bool) -> None:
+        entry = self._pending.get(block)
+        if entry is None:
+            return
+        ev, host, step = entry
+        if not wait and not ev.query():
+            return
+        ev.synchronize()
+        del self._pending[block]
+        if int(host[0]) != 0:
+            raise RuntimeError(f"the plan of block {block} built at step {step} outgrew its "
+                               "capacity (its attention calls returned zeros)")
+
+    def check(self) -> None:
+        """Waits for every plan-status check in flight; raises on an overflow."""
+        for block in list(self._pending):
+            self._check_block(block, wait=True)
 
     def problem(self, q: torch.Tensor) -> Problem:
         return Problem.like(q, n_forced_tail=self.n_text, n_clusters=self.n_clusters,
@@ -125,6 +151,8 @@ class ABAttention:
 
     def __call__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
                  return_lse: bool = False):
+        for b in list(self._pending):       # completed checks only: no host stall
+            self._check_block(b, wait=False)
         mode = self.policy.mode(self.step, block)
         prob = self.problem(q)
         if mode == REUSE:
@@ -137,10 +165,17 @@ class ABAttention:
         if mode == BUILD:
             old = self._plans.get(block)
             reuse_buf = old[1] if old is not None and old[2] == prob else None
+            self._check_block(block, wait=True)   # the last build's copy (long finished)
             pl = plan(q, k, self.policy.budget, seed=self.policy.seed(self.step, block),
                       problem=prob, out=reuse_buf)
-            if not pl.ok():
-                raise RuntimeError("plan outgrew its capacity")
+            host = self._status_host.get(block)
+            if host is None:
+                host = torch.empty(1, dtype=torch.int32, pin_memory=True)
+                self._status_host[block] = host
+            host.copy_(pl.status, non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record()
+            self._pending[block] = (ev, host, self.step)
             self._plans[block] = (self.step, pl, prob)
         if self.fp16_v and v.dtype == torch.bfloat16:
             if self._v16 is None or self._v16.shape != v.shape or self._v16.device != v.device:

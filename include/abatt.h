@@ -46,6 +46,11 @@
  *     scored and are kept in every plan row with weight 1.
  *   - Plan row r belongs to (b, h, qb) with r = (b*H + h)*n_qb + qb,
  *     n_qb = ceil(N / q_block).
+ *   - Inputs must be finite.  The attention kernels are built without IEEE
+ *     NaN semantics (NaN-propagating max and compare are dropped from the
+ *     softmax), and the selector's scores and sampler assume finite values:
+ *     NaN or Inf anywhere in Q, K or V gives unspecified (but in-bounds)
+ *     results.  Nothing checks this on the device.
  */
 #ifndef ABATT_H
 #define ABATT_H

@@ -167,12 +167,12 @@ def query_clusters(Q: np.ndarray, prob: Problem, rows: Optional[List[int]] = Non
 
 
 def block_scores(mu: np.ndarray, w: np.ndarray, kbar: np.ndarray, tau: float) -> np.ndarray:
-    """Cluster-weighted attention of one block's centroids to the key means.
+    """s_j = sum_c w_c softmax_j(tau * mu_c . kbar_j) over the sparse key blocks j.
 
-    [hamidun] three techniques, IBCS: a key block's score is the weighted
-    attention of the centroids to its averaged keys.  Each centroid's
-    attention is a softmax over all sparse key blocks (logit = tau * mu.kbar);
-    the weights are the cluster shares.  Returns float64 [n_kbs].
+    [hamidun] three techniques, IBCS.  Every centroid mu_c of the query
+    block spreads one softmax over the means kbar_j of all sparse key blocks;
+    the block scores are those probabilities summed with the cluster shares
+    w_c as weights (so they sum to 1).  Returns float64 [n_kbs].
     """
     logits = tau * (mu @ kbar.T)                        # [C, n_kbs]
     shifted = logits - logits.max(axis=1, keepdims=True)
@@ -211,9 +211,9 @@ def ibcs_scores(Q: np.ndarray, K: np.ndarray, prob: Problem,
 def inclusion_probabilities(s32: np.ndarray, budget: float) -> np.ndarray:
     """pi_j proportional to the score, capped at 1, summing to the budget.
 
-    [hamidun] three techniques, SIP: a block is sampled with probability
-    proportional to its score; the most important blocks are certain (pi=1)
-    and every other block keeps a nonzero chance.  With m = budget * n
+    [hamidun] three techniques, SIP: pi scales with the block's score, is
+    capped at 1 for the top-scored blocks (always drawn), and stays above zero
+    for every other block with a positive score.  With m = budget * n
     expected blocks, start with no certain blocks and repeat: c = (m - #certain)
     / (sum of the scores of the uncertain positive blocks); every uncertain
     block with c*s >= 1 becomes certain; stop when none does.  Then pi = 1 on

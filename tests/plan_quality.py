@@ -5,10 +5,11 @@ What is compared (news.hamidun.com, "AB-Attention speeds up video generation
 by up to 2.23x and skips 92% of attention"):
   * section "Where earlier sparse schemes break down": ideal top-k selection
     keeps only part of the attention mass (about 69% at 10.8% of the keys);
-  * section "AB-Attention's three techniques": IBCS halves the recall gap
-    between block averaging and ideal top-k; SIP's attention error is 41%
-    below ideal top-k at the same number of blocks; 4-token blocks keep more
-    mass than 128-token blocks under ideal selection (69% against 59%).
+  * section "AB-Attention's three techniques": against ideal top-k, IBCS
+    leaves half the recall shortfall of mean-pooled block scoring; with equally
+    many blocks, SIP's output error is 41% smaller than ideal top-k's; under
+    ideal selection 4-token blocks retain 69% of the mass against 59% for
+    128-token blocks.
 Those figures come from real model activations; on the synthetic inputs here
 they are context, not targets (parity unpinned).
 

@@ -4,7 +4,7 @@ host logic on the CPU, the attention callable on the GPU.
 Pins: the schedule the pages describe (news.hamidun.com, "AB-Attention speeds
 up video generation by up to 2.23x and skips 92% of attention": the plan is
 rebuilt every four denoising steps, section "AB-Attention's three techniques";
-the first block and the first 10 of 50 steps run dense, section "How it was
+dense attention in block 0 at every step and in steps 0-9 of 50, section "How it was
 measured and what came out"), counted by hand for a 50-step, 40-block run;
 SplitMix64 against its published first outputs for state 0 (Steele et al.,
 OOPSLA 2014; the sequence of Vigna's reference generator seeded with 0).
@@ -121,3 +121,34 @@ def test_attention_callable_in_a_denoising_loop():
     assert {m: modes.count(m) for m in (DENSE, BUILD, REUSE)} == pol.counts(n_blocks)
     assert pol.counts(n_blocks) == {DENSE: 2 * 3 + 10, BUILD: 3 * 2, REUSE: 7 * 2}
     assert len(plans) == 6
+
+
+@pytest.mark.gpu
+def test_overflowed_plan_raises_without_a_stall_per_build():
+    """A plan that outgrows its capacity still raises: at the next call once
+    its status copy has landed, or at check() (which waits)."""
+    import block_sparse_attention_09_amd as ab
+    from helpers import say, to_dev
+    from workloads import Workload, make_qkv
+
+    wl = Workload("ovf", B=1, H=1, D=128, grid=(2, 8, 16))
+    q, k, v = make_qkv(wl)
+    dq, dk, dv = (to_dev(x, "bf16") for x in (q, k, v))
+    pol = StepPolicy(total_steps=4, dense_steps=0, dense_blocks=0, plan_every=4, budget=0.5)
+    for via_check in (False, True):
+        attn = ABAttention(pol)
+        prob = attn.problem(dq)
+        # a cached plan of this problem with room for one entry: the build at
+        # step 0 writes into it and overflows
+        attn._plans[0] = (-1, ab.empty_plan(prob, 1, dq.device), prob)
+        attn.set_step(0)
+        say(f"policy overflow (check() {via_check})")
+        o = attn(dq, dk, dv, 0)                      # deferred: no raise yet
+        torch.cuda.synchronize()
+        assert int(attn.plan_of(0).status.item()) == 1
+        assert torch.count_nonzero(o) == 0           # every row empty
+        with pytest.raises(RuntimeError, match="outgrew its capacity"):
+            if via_check:
+                attn.check()
+            else:
+                attn(dq, dk, dv, 1)                  # the next call surfaces it
