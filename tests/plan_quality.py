@@ -35,7 +35,12 @@ from typing import Dict, Iterable, List, Optional
 
 import numpy as np
 
-import oracle
+if __name__ == "__main__":   # run as a script: oracle/ and workloads/ sit at the repo root
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+import oracle  # noqa: E402
 
 
 @dataclasses.dataclass
@@ -165,3 +170,44 @@ REPORT_HEADER = [
     "IBCS gap / avg gap | err ideal top-k | err SIP | SIP / ideal | ideal recall K_b=4 | "
     "ideal recall K_b=128 |",
     "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+
+
+def sweep(amps, budgets, nrows: int = 24, workload: str = "wan1p3b_480p",
+          v_pe: float = 0.0) -> List[str]:
+    """Markdown table of the harness over position-code amplitudes and budgets
+    on one head of a workload, with the oracle's own plans (plans from the
+    library agree with them on >= 99.9% of blocks); v_pe gives the values a
+    positional structure of that amplitude (workloads' v_pe_amp)."""
+    from workloads import CONFIGS, make_qkv
+    lines = list(REPORT_HEADER) + ["|" + " --- |" * 12]
+    for a in amps:
+        wl = CONFIGS[workload].scaled(H=1, pe_amp=a, v_pe_amp=v_pe)
+        q, k, v = make_qkv(wl)
+        prob = oracle.Problem(B=1, H=1, N=wl.N, D=wl.D, n_clusters=wl.n_clusters,
+                              kmeans_iters=wl.kmeans_iters, n_forced_tail=wl.n_text)
+        rows = list(np.linspace(0, prob.R - 1, nrows).astype(int))
+        sc = oracle.ibcs_scores(q, k, prob, rows=rows)
+        for budget in budgets:
+            pl = oracle.plan_from_scores(sc["S32"], prob, budget, wl.plan_seed, rows)
+            res = evaluate(q, k, v, prob, pl, rows, ibcs_scores=sc["S"])
+            by = ideal_recall_by_block_size(q, k, prob, rows, res["key_fraction"])
+            tag = f"{workload} H=1 pe_amp={a}" + (f" v_pe={v_pe}" if v_pe else "")
+            lines += report(f"{tag}, budget {budget}, {nrows} rows", res, by)
+            print(lines[-1], flush=True)
+    return lines
+
+
+if __name__ == "__main__":
+    import argparse
+    ap = argparse.ArgumentParser(description="plan-quality sweep (oracle plans, CPU)")
+    ap.add_argument("--amps", default="4,5,6")
+    ap.add_argument("--budgets", default="0.05,0.1,0.2")
+    ap.add_argument("--rows", type=int, default=24)
+    ap.add_argument("--workload", default="wan1p3b_480p")
+    ap.add_argument("--v-pe", type=float, default=0.0,
+                    help="amplitude of the positional structure in v (0: v is pure noise)")
+    args = ap.parse_args()
+    out = sweep([float(x) for x in args.amps.split(",")],
+                [float(x) for x in args.budgets.split(",")], args.rows, args.workload,
+                args.v_pe)
+    print("\n".join(out))

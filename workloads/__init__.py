@@ -23,6 +23,9 @@ Recipe (per config):
     i = (t*H_g + y)*W_g + x.
   * q = sigma*z_q + PE, k = sigma*z_k + PE, v = z_v.  Text tokens (appended at
     the tail, HunyuanVideo shape only) get q, k = sigma*z with no PE.
+  * Optional (plan-quality sweeps only; 0 everywhere else): v also gets
+    v_pe_amp * PE with its dimensions rotated by D/2, a smooth positional
+    structure in the values that is not a copy of q's and k's.
   * bf16 configs round the float32 values to bfloat16 (round to nearest even);
     both sides of any comparison see the same bits.
 """
@@ -59,6 +62,7 @@ class Workload:
     drift: float = 0.0                  # per-call q/k drift std when reused
     pe_amp: float = 1.0                 # amplitude of the position code (1 everywhere
                                         # except the plan-quality sweep)
+    v_pe_amp: float = 0.0               # positional structure in v (plan-quality sweep)
 
     @property
     def N(self) -> int:
@@ -156,6 +160,9 @@ class Generator:
         k = s * zk
         q[:nv] += self.pe
         k[:nv] += self.pe
+        if wl.v_pe_amp:
+            zv[:nv] += np.float32(wl.v_pe_amp / wl.pe_amp if wl.pe_amp else 0.0) * \
+                np.roll(self.pe, d // 2, axis=1)
         return q, k, zv
 
     def iter_heads(self) -> Iterator[Tuple[int, int, np.ndarray, np.ndarray, np.ndarray]]:
