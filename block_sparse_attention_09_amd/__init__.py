@@ -32,6 +32,7 @@ SYMBOLS = (
     "abatt_plan_rows", "abatt_plan_max_nnz", "abatt_plan_nnz_bound",
     "abatt_plan_workspace_bytes", "abatt_sampler_workspace_bytes", "abatt_plan",
     "abatt_plan_noalloc", "abatt_attend", "abatt_v_to_f16", "abatt_attend_v16", "abatt_dense",
+    "abatt_dense_v16",
     "abatt_key_means", "abatt_scores", "abatt_plan_from_scores", "abatt_status_str",
     "abatt_version",
 )
@@ -79,6 +80,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "abatt_v_to_f16": (st, [P, vp, vp, vp]),
         "abatt_attend_v16": (st, [P, vp, vp, vp, ctypes.POINTER(_Plan), vp, vp, vp]),
         "abatt_dense": (st, [P, vp, vp, vp, vp, vp, vp]),
+        "abatt_dense_v16": (st, [P, vp, vp, vp, vp, vp, vp]),
         "abatt_key_means": (st, [P, vp, vp, vp]),
         "abatt_scores": (st, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
         "abatt_plan_from_scores": (st, [P, vp, ctypes.c_double, ctypes.c_uint64, vp, sz,
@@ -360,9 +362,17 @@ def attend(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pl: Plan,
 
 def dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, problem: Optional[Problem] = None,
           return_lse: bool = False, out: Optional[torch.Tensor] = None):
-    """Dense softmax attention over every key (abatt_dense)."""
+    """Dense softmax attention over every key (abatt_dense).
+
+    A float16 `v` (from v_to_f16) selects abatt_dense_v16, with bit-identical results.
+    """
     prob = problem or Problem.like(q)
-    _qkv_check(prob, q, k, v)
+    v16 = v.dtype == torch.float16
+    _qkv_check(prob, q, k)
+    if v16:
+        _v16_check(prob, v)
+    else:
+        _qkv_check(prob, v)
     for t in (k, v):
         if t.device != q.device:
             raise ValueError(f"q, k and v must be on one device ({q.device}, {t.device})")
@@ -373,8 +383,8 @@ def dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, problem: Optional[P
         o = out
     lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32, device=q.device) \
         if return_lse else None
-    _check(load_library().abatt_dense(ctypes.byref(prob.c()), _ptr(q), _ptr(k), _ptr(v),
-                                      _ptr(o), _ptr(lse), _stream()))
+    fn = load_library().abatt_dense_v16 if v16 else load_library().abatt_dense
+    _check(fn(ctypes.byref(prob.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream()))
     return (o, lse) if return_lse else o
 
 

@@ -274,8 +274,9 @@ abatt_status abatt_attend(const abatt_problem_t* p, const void* Q, const void* K
 
 abatt_status abatt_v_to_f16(const abatt_problem_t* p, const void* V, void* V16,
                             hipStream_t stream) {
+  // an elementwise conversion: any N (as for dense attention) is fine
   Shape s;
-  abatt_status st = make_shape(p, &s);
+  abatt_status st = make_dense_shape(p, &s);
   if (st != ABATT_OK) return st;
   if (!s.bf16) return ABATT_EUNSUPPORTED;
   if (bad(V) || bad(V16) || V == V16) return ABATT_EINVAL;
@@ -305,6 +306,17 @@ abatt_status abatt_dense(const abatt_problem_t* p, const void* Q, const void* K,
   if (bad(Q) || bad(K) || bad(V) || bad(O)) return ABATT_EINVAL;
   return hip_status(abatt::launch_attend(s, Q, K, V, nullptr, nullptr, nullptr, 0, nullptr, O,
                                          lse, false, false, stream));
+}
+
+abatt_status abatt_dense_v16(const abatt_problem_t* p, const void* Q, const void* K,
+                             const void* V16, void* O, float* lse, hipStream_t stream) {
+  Shape s;
+  abatt_status st = make_dense_shape(p, &s);
+  if (st != ABATT_OK) return st;
+  if (!s.bf16) return ABATT_EUNSUPPORTED;
+  if (bad(Q) || bad(K) || bad(V16) || bad(O)) return ABATT_EINVAL;
+  return hip_status(abatt::launch_attend(s, Q, K, V16, nullptr, nullptr, nullptr, 0, nullptr, O,
+                                         lse, false, true, stream));
 }
 
 const char* abatt_status_str(abatt_status s) {

@@ -102,8 +102,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base
                                            0x00020000);
 }
 
-// kV16: V arrives already converted to fp16 (gathered rows only) and goes
-// to LDS by direct loads like K.
+// kV16: V arrives already converted to fp16.  Gathered rows move it to LDS
+// by direct loads like K; dense rows stage it through registers unconverted.
 template <int D, bool kGather, bool kV16>
 __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -118,7 +118,6 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   constexpr int BPS = 64 / (4 * CPR); // 4-key groups covered by one wave-wide load (1 or 2)
   constexpr int GROUP_BYTES = 4 * D * 2;  // one group of 4 keys
   static_assert(SLOTS * BPS == 4, "a wave moves 4 groups of each chunk");
-  static_assert(kGather || !kV16, "fp16 V is a gathered-row form");
   // K tile: row-major, 16-byte slot s of row r stored at s ^ (r % CPR)
   // (conflict-free operand reads without padding; the direct loads place each
   // lane's 16 bytes at a fixed LDS position, so the swizzle is chosen through
@@ -209,7 +208,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   // Gathered rows: K goes straight to LDS, V through registers (converted to
   // fp16 on its way to LDS).  Dense rows stage K through registers too
   // (measured faster there).
-  u32x4 vpre[kV16 ? 1 : SLOTS], kpre[kGather ? 1 : SLOTS];
+  u32x4 vpre[kGather && kV16 ? 1 : SLOTS], kpre[kGather ? 1 : SLOTS];
   int id_next = 0;                   // raw ids of the next chunk to start (gathered rows)
   float lw_next = 0.f;
 
@@ -265,7 +264,8 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     }
   };
   // The chunk in registers into stage buf: V converted to fp16 (exact for
-  // bf16 values in fp16's normal range); dense rows: K as well.
+  // bf16 values in fp16's normal range; as it is with fp16 V); dense rows: K
+  // as well.
   auto store_regs = [&](int buf) {
     uint16_t* vst = Vs[buf];
 #pragma unroll
@@ -274,10 +274,14 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
       if constexpr (!kGather)
         *reinterpret_cast<u32x4*>(&Ks[buf][row * D + 8 * (dc ^ (row % CPR))]) = kpre[i];
       u32x4 hv;
+      if constexpr (kV16) {
+        hv = vpre[i];
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        hv[e] = pack_f16_rtz(__uint_as_float(vpre[i][e] << 16),
-                             __uint_as_float(vpre[i][e] & 0xffff0000u));
+        for (int e = 0; e < 4; ++e)
+          hv[e] = pack_f16_rtz(__uint_as_float(vpre[i][e] << 16),
+                               __uint_as_float(vpre[i][e] & 0xffff0000u));
+      }
       *reinterpret_cast<u32x4*>(&vst[row * D + 8 * (dc ^ vswz<D>(row))]) = hv;
     }
   };
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     } else {
       issue_dense(0);
     }
-    if constexpr (!kV16) store_regs(0);
+    if constexpr (!(kGather && kV16)) store_regs(0);
     if constexpr (!kGather) issue_dense(min(1, clast));
   }
   dma_barrier();
@@ -644,9 +648,12 @@ hipError_t launch_attend(const Shape& s, const void* Q, const void* K, const voi
                          int64_t capacity, const int32_t* status, void* O, float* lse,
                          bool gather, bool v16, hipStream_t st) {
 #define ABATT_ATTEND(Dv)                                                                     \
-  if (v16)                                                                                   \
+  if (v16 && gather)                                                                         \
     launch_attend_t<Dv, true, true>(s, Q, K, V, row_ptr, col_idx, logw, capacity, status, O, \
                                     lse, st);                                                \
+  else if (v16)                                                                              \
+    launch_attend_t<Dv, false, true>(s, Q, K, V, row_ptr, col_idx, logw, capacity, status,   \
+                                     O, lse, st);                                            \
   else if (gather)                                                                           \
     launch_attend_t<Dv, true, false>(s, Q, K, V, row_ptr, col_idx, logw, capacity, status,   \
                                      O, lse, st);                                            \

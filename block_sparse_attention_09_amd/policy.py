@@ -97,10 +97,10 @@ class ABAttention:
     event, and checked at the next call once that event has completed (and at
     the block's next build, or by ``check()``, which waits).  An overflowed
     plan makes attention return zeros for the calls made before the error
-    surfaces.  For bf16 inputs the sparse
-    calls convert V to fp16 once per call and use the attention's fp16-V form
-    (abatt_v_to_f16 + abatt_attend_v16: the same results, a faster kernel)
-    unless ``fp16_v`` is False.
+    surfaces.  For bf16 inputs every call converts V to fp16 once and uses
+    the attention's fp16-V forms (abatt_v_to_f16 + abatt_attend_v16 or
+    abatt_dense_v16: the same results, faster kernels) unless ``fp16_v`` is
+    False.
     """
 
     def __init__(self, policy: StepPolicy = StepPolicy(), n_text: int = 0,
@@ -160,6 +160,10 @@ class ABAttention:
             if entry is None or entry[2] != prob:
                 mode = BUILD   # no usable plan (first call after a skipped build, or new shape)
         self.log.append((self.step, block, mode))
+        if self.fp16_v and v.dtype == torch.bfloat16:
+            if self._v16 is None or self._v16.shape != v.shape or self._v16.device != v.device:
+                self._v16 = torch.empty(v.shape, dtype=torch.float16, device=v.device)
+            v = v_to_f16(v, prob, out=self._v16)
         if mode == DENSE:
             return dense(q, k, v, problem=prob, return_lse=return_lse)
         if mode == BUILD:
@@ -177,8 +181,4 @@ class ABAttention:
             ev.record()
             self._pending[block] = (ev, host, self.step)
             self._plans[block] = (self.step, pl, prob)
-        if self.fp16_v and v.dtype == torch.bfloat16:
-            if self._v16 is None or self._v16.shape != v.shape or self._v16.device != v.device:
-                self._v16 = torch.empty(v.shape, dtype=torch.float16, device=v.device)
-            v = v_to_f16(v, prob, out=self._v16)
         return attend(q, k, v, self._plans[block][1], problem=prob, return_lse=return_lse)

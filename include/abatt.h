@@ -220,7 +220,8 @@ abatt_status abatt_attend(const abatt_problem_t *p, const void *Q, const void *K
  * on the V that V16 came from.
  *
  * V, V16: [B,H,N,D] device buffers of 2-byte elements, caller-owned; V16 is
- * written in full and must not be V.  Other arguments as abatt_attend.
+ * written in full and must not be V.  abatt_v_to_f16 checks the problem as
+ * abatt_dense does (any N; kv_block and n_forced_tail are not used).  Other arguments as abatt_attend.
  * Returns ABATT_EUNSUPPORTED for fp32 problems, and ABATT_EINVAL for NULL
  * pointers or V16 == V.
  */
@@ -238,6 +239,16 @@ abatt_status abatt_attend_v16(const abatt_problem_t *p, const void *Q, const voi
  */
 abatt_status abatt_dense(const abatt_problem_t *p, const void *Q, const void *K,
                          const void *V, void *O, float *lse, hipStream_t stream);
+
+/*
+ * abatt_dense_v16 -- abatt_dense with V given as fp16 (from abatt_v_to_f16),
+ * for bf16 problems: the dense kernel then stages V as it is instead of
+ * converting each chunk for every query block.  O and lse are bit-identical to
+ * abatt_dense's on the V that V16 came from.  Same checks as abatt_dense;
+ * ABATT_EUNSUPPORTED for fp32 problems.
+ */
+abatt_status abatt_dense_v16(const abatt_problem_t *p, const void *Q, const void *K,
+                             const void *V16, void *O, float *lse, hipStream_t stream);
 
 /*
  * Test hooks: the selector's kernels entered part-way.

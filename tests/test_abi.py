@@ -130,7 +130,10 @@ def test_argument_checks_before_any_hip_call(lib):
     assert lib.abatt_v_to_f16(P(c), fake, fake, None) == -1
     assert lib.abatt_attend_v16(P(c), fake, fake, None, P(good), fake, None, None) == -1
     assert lib.abatt_attend_v16(P(c), fake, fake, fake, P(noarr), fake, None, None) == -1
+    assert lib.abatt_dense_v16(P(c), fake, fake, None, fake, None, None) == -1
+    assert lib.abatt_dense_v16(P(c), fake, fake, odd, fake, None, None) == -1
     c32 = prob(dtype="f32", D=64).c()
+    assert lib.abatt_dense_v16(P(c32), fake, fake, fake, fake, None, None) == -2
     assert lib.abatt_v_to_f16(P(c32), fake, ctypes.c_void_p(0x2000), None) == -2
     assert lib.abatt_attend_v16(P(c32), fake, fake, fake, P(good), fake, None, None) == -2
     # dense accepts N not a multiple of 4 (keys past N are masked) but still checks D

@@ -1,4 +1,5 @@
-"""The fp16-V form of the gathered attention: abatt_v_to_f16 + abatt_attend_v16.
+"""The fp16-V forms of the attention: abatt_v_to_f16, then abatt_attend_v16
+(gathered rows) or abatt_dense_v16 (every key).
 
 * the conversion against an independent reference: bf16 -> fp16 rounded
   toward zero (NumPy's round-to-nearest, stepped one fp16 ulp toward zero
@@ -7,7 +8,10 @@
 * attention on the converted V is bit-identical to abatt_attend on the bf16 V
   (output and log-sum-exp), for D = 128 and 64, several key-block sizes, text
   tokens, and values beyond fp16's range;
-* and against the oracle, at the bf16 bar (max-abs 1e-2, mean-rel 1e-3).
+* and against the oracle, at the bf16 bar (max-abs 1e-2, mean-rel 1e-3);
+* dense attention on the converted V is bit-identical to abatt_dense (output
+  and log-sum-exp), for D = 128 and 64 and token counts that are not a
+  multiple of the 64-key chunk or of 4.
 """
 import numpy as np
 import pytest
@@ -124,3 +128,18 @@ def test_v16_rejects_fp32_and_wrong_shapes():
     with pytest.raises(ValueError):
         ab.v_to_f16(torch.zeros(1, 1, 256, 64, dtype=torch.bfloat16, device="cuda"), pb,
                     out=torch.empty(1, 1, 256, 32, dtype=torch.float16, device="cuda"))
+
+
+@pytest.mark.parametrize("D,N", [(128, 2048), (128, 1150), (64, 1027), (64, 300)])
+def test_dense_v16_is_bit_identical(D, N):
+    rng = np.random.default_rng(D + N)
+    q, k, v = (round_like(rng.standard_normal((1, 2, N, D)).astype(np.float32), "bf16")
+               for _ in range(3))
+    prob = ab.Problem(1, 2, N, D)
+    dq, dk, dv = (to_dev(x, "bf16") for x in (q, k, v))
+    say(f"dense fp16-V D={D} N={N}")
+    o, lse = ab.dense(dq, dk, dv, problem=prob, return_lse=True)
+    o16, lse16 = ab.dense(dq, dk, ab.v_to_f16(dv, prob), problem=prob, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o)
+    assert torch.equal(lse16, lse)
