@@ -43,6 +43,19 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
+PROBE_SRC = os.path.join(CSRC, "mfma_probe.hip")
+PROBE = os.path.join(PKG, "mfma_probe")
+
+
+def build_probe() -> str:
+    """The MFMA issue probe (a measurement program, not part of libabatt)."""
+    cmd = [HIPCC, *FLAGS, PROBE_SRC, "-o", PROBE]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for mfma_probe.hip:\n{r.stderr}")
+    return PROBE
+
+
 def build(verbose: bool = False, extra=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(6, os.cpu_count() or 1)) as ex:
@@ -53,8 +66,9 @@ def build(verbose: bool = False, extra=()) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe()
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE}")
     return LIB
 
 
