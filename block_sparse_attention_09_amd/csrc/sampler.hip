@@ -15,10 +15,10 @@
 //     set of the scores, so it is held as a threshold theta (certain iff
 //     s >= theta).  float64 throughout; sums are fixed-order tree reductions,
 //     so every run gives the same bits.
-//   * draws: block j uses words 2(j%2), 2(j%2)+1 of Philox4x32-10 with
-//     counter (j/2, qb, h, b) and key (seed low, seed high) as one 53-bit
-//     uniform (32 bits from the first word, the top 21 of the second); kept
-//     iff it is < pi_j * 2^53 (exact compare).
+//   * draws: block j uses word j%4 of Philox4x32-10 with counter
+//     (j/4, qb, h, b) and key (seed low, seed high) as a 32-bit uniform
+//     integer w; kept iff w < pi_j * 2^32 (exact compare), so it enters with
+//     probability ceil(pi_j * 2^32) / 2^32, within 2^-32 of pi_j.
 // k_sip_count solves pi, draws, and records the row's kept-block bitmask, its
 // count and its solve (mode, c, theta); k_scan turns counts into row_ptr (and
 // flags a plan that exceeds its capacity); k_sip_fill walks the bitmask and
@@ -226,24 +226,17 @@ __device__ __forceinline__ double pi_x32(float s, const PiSolve& ps, double c32)
   return c32 * (double)s;
 }
 
-// Kept-bit mask (4 bits) of blocks 4g..4g+3: two Philox calls (counters 2g
-// and 2g+1), each giving two 53-bit uniforms u = w0 * 2^21 + (w1 >> 11)
-// (words 0,1 and 2,3); kept iff u < pi * 2^53, decided by sip_keep
-// (draw_rule.h) on the first word except on a tie.
+// Kept-bit mask (4 bits) of blocks 4g..4g+3: one Philox call (counter g),
+// word k for block 4g + k.
 __device__ __forceinline__ uint32_t draw_group(const float* s, int n, int g, int qb, int h, int b,
                                                uint64_t seed, const PiSolve& ps, double c32) {
+  uint32_t c[4] = {(uint32_t)g, (uint32_t)qb, (uint32_t)h, (uint32_t)b};
+  philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
   uint32_t mask = 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    uint32_t c[4] = {(uint32_t)(2 * g + i), (uint32_t)qb, (uint32_t)h, (uint32_t)b};
-    philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int j = 4 * g + 2 * i + k;
-      if (j < n) {
-        if (sip_keep(c[2 * k], c[2 * k + 1], pi_x32(s[j], ps, c32))) mask |= 1u << (2 * i + k);
-      }
-    }
+  for (int k = 0; k < 4; ++k) {
+    const int j = 4 * g + k;
+    if (j < n && sip_keep(c[k], pi_x32(s[j], ps, c32))) mask |= 1u << k;
   }
   return mask;
 }

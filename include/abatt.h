@@ -142,9 +142,10 @@ size_t abatt_sampler_workspace_bytes(const abatt_problem_t *p);
  *      operands (fp32 problems); accumulation and softmax are fp32;
  *   4. inclusion probability pi_j proportional to s_j, capped at 1, summing
  *      to m = budget * n_kbs per row (float64 water-filling);
- *   5. block j kept iff the 53-bit uniform made of words 2(j%2) (32 bits)
- *      and 2(j%2)+1 (top 21 bits) of Philox4x32-10(counter (j/2, qb, h, b),
- *      key (seed low, seed high)) is below pi_j * 2^53;
+ *   5. block j kept iff word j%4 of Philox4x32-10(counter (j/4, qb, h, b),
+ *      key (seed low, seed high)), a 32-bit uniform integer, is below
+ *      pi_j * 2^32 (exact compare: inclusion probability within 2^-32 of
+ *      pi_j);
  *   6. CSR rows in ascending block order, logw = log(1/pi) rounded to fp32
  *      (0 where pi = 1), forced blocks appended with logw 0.
  * budget in (0, 1]; budget 1 keeps every block.  Q, K: [B,H,N,D] device.

@@ -8,4 +8,4 @@ from .abatt_oracle import (Problem, Plan, attend, attend_row, dense, dense_rows,
                            ht_estimates, ibcs_scores, inclusion_probabilities,
                            key_block_means, kmeans, philox4x32_10, plan,
                            plan_from_scores, query_clusters, sample_row,
-                           block_scores, block_uniforms, unflatten_row)
+                           block_scores, block_words, unflatten_row)

@@ -28,9 +28,10 @@ the design notes):
     normalised per centroid over the sparse key blocks, then rounded to fp32;
   * budget b means m = b * n_sparse_blocks expected blocks per row; b = 1
     takes every block; independent (Poisson) draws, so the row count varies;
-  * randomness: Philox4x32-10, counter (j//2, qb, h, b), key (seed low,
-    seed high), words 2(j%2) and 2(j%2)+1 as one 53-bit uniform compared
-    exactly against pi * 2^53;
+  * randomness: Philox4x32-10, counter (j//4, qb, h, b), key (seed low,
+    seed high); word j%4 is block j's 32-bit uniform integer w, and the
+    block is kept iff w < pi * 2^32 (exact in float64), so it enters with
+    probability ceil(pi * 2^32) / 2^32, within 2^-32 of pi;
   * trailing text tokens (if any) form forced key blocks with pi = 1 that are
     not scored and not counted in the budget.
 
@@ -271,21 +272,16 @@ def philox4x32_10(ctr: Tuple[np.ndarray, ...], key: Tuple[int, int]) -> Tuple[np
     return c0, c1, c2, c3
 
 
-def block_uniforms(b: int, h: int, qb: int, n: int, seed: int) -> np.ndarray:
-    """53-bit uniform integers (uint64) for sparse key blocks 0..n-1 of a row.
-
-    Block j uses words 2(j%2) and 2(j%2)+1 of Philox4x32-10 with counter
-    (j//2, qb, h, b) and key (low, high 32 bits of the seed): the first word
-    gives the top 32 bits, the top 21 bits of the second the rest.
-    """
-    pairs = -(-n // 2)
-    g = np.arange(pairs, dtype=np.uint64)
-    z = np.zeros(pairs, dtype=np.uint64)
-    w0, w1, w2, w3 = philox4x32_10((g, z + np.uint64(qb), z + np.uint64(h), z + np.uint64(b)),
-                                   (seed & M32, (seed >> 32) & M32))
-    hi = np.stack([w0, w2], axis=1).reshape(-1)[:n]
-    lo = np.stack([w1, w3], axis=1).reshape(-1)[:n]
-    return (hi << np.uint64(21)) | (lo >> np.uint64(11))
+def block_words(b: int, h: int, qb: int, n: int, seed: int) -> np.ndarray:
+    """32-bit uniform integers (uint64 holding values < 2^32) for sparse key
+    blocks 0..n-1 of a row: block j is word j%4 of Philox4x32-10 with counter
+    (j//4, qb, h, b) and key (low, high 32 bits of the seed)."""
+    quads = -(-n // 4)
+    g = np.arange(quads, dtype=np.uint64)
+    z = np.zeros(quads, dtype=np.uint64)
+    w = philox4x32_10((g, z + np.uint64(qb), z + np.uint64(h), z + np.uint64(b)),
+                      (seed & M32, (seed >> 32) & M32))
+    return np.stack(w, axis=1).reshape(-1)[:n]
 
 
 def sample_row(s32: np.ndarray, budget: float, b: int, h: int, qb: int, seed: int,
@@ -294,14 +290,14 @@ def sample_row(s32: np.ndarray, budget: float, b: int, h: int, qb: int, seed: in
 
     [hamidun] three techniques, SIP: each block enters independently with
     probability pi; a kept block is weighted by 1/pi (Horvitz-Thompson),
-    applied as the logit shift log(1/pi).  Block j is kept iff its 53-bit
-    uniform u satisfies u < pi * 2^53 (exact in float64).  Forced blocks
-    (ids n..n+n_forced_blocks-1) are always kept with weight 1.
+    applied as the logit shift log(1/pi).  Block j is kept iff its 32-bit
+    uniform integer w satisfies w < pi * 2^32 (exact in float64).  Forced
+    blocks (ids n..n+n_forced_blocks-1) are always kept with weight 1.
     """
     n = s32.shape[0]
     pi = inclusion_probabilities(s32, budget)
-    u = block_uniforms(b, h, qb, n, seed).astype(np.float64)
-    keep = u < pi * float(1 << 53)
+    w = block_words(b, h, qb, n, seed).astype(np.float64)
+    keep = w < pi * float(1 << 32)
     idx = np.nonzero(keep)[0]
     pik = pi[idx]
     lw = np.where(pik == 1.0, 0.0, -np.log(np.where(pik == 1.0, 1.0, pik)))

@@ -1,18 +1,18 @@
 // Host harness of the sampler's keep decision: the sampler kernel's own
-// sip_keep (draw_rule.h), compiled for the host.  Reads lines
-// "x_bits w0 w1" -- the float64 bits of x = pi * 2^32 in hex, then the two
-// Philox words in decimal -- and prints 1 (kept) or 0 per line.
+// sip_keep (draw_rule.h), compiled for the host.  Reads lines "x_bits w" --
+// the float64 bits of x = pi * 2^32 in hex, then the Philox word in decimal --
+// and prints 1 (kept) or 0 per line.
 #include <cstdio>
 #include <cstring>
 
 #include "../block_sparse_attention_09_amd/csrc/draw_rule.h"
 
 int main() {
-  unsigned long long bits, w0, w1;
-  while (std::scanf("%llx %llu %llu", &bits, &w0, &w1) == 3) {
+  unsigned long long bits, w;
+  while (std::scanf("%llx %llu", &bits, &w) == 2) {
     double x;
     std::memcpy(&x, &bits, sizeof x);
-    std::printf("%d\n", abatt::sip_keep((uint32_t)w0, (uint32_t)w1, x) ? 1 : 0);
+    std::printf("%d\n", abatt::sip_keep((uint32_t)w, x) ? 1 : 0);
   }
   return 0;
 }

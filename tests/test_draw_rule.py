@@ -1,13 +1,12 @@
-"""The sampler's draw compare, decided on the first Philox word.
+"""The sampler's draw compare on the shipped code.
 
-A block is kept iff its 53-bit uniform u = w0 * 2^21 + (w1 >> 11) is below
-pi * 2^53.  The GPU decides on w0 alone unless w0 equals
-f = floor(min(pi * 2^32, 2^32 - 1)), and takes the exact compare only then.
-The kernel's own decision function (sip_keep in csrc/draw_rule.h, which the
+A block is kept iff its 32-bit uniform integer w (one Philox word) is below
+pi * 2^32, so it enters with probability ceil(pi * 2^32) / 2^32.  The
+kernel's own decision function (sip_keep in csrc/draw_rule.h, which the
 sampler kernel calls) is compiled for the host into a small harness and
-checked against the exact rational comparison, including the ties
-(probability 2^-32 per block, so the GPU tests never reach them), pi = 0,
-pi = 1 and values of pi * 2^32 within one step of 2^32.
+checked against the exact rational comparison: pi = 0 and 1, pi * 2^32 on
+and next to an integer, the ends of the word range, and random cases.  The
+oracle's rule is checked against the same exact comparison.
 """
 import os
 import shutil
@@ -18,10 +17,11 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
+import oracle
 
-def exact_keep(pi: float, w0: int, w1: int) -> bool:
-    u = (w0 << 21) | (w1 >> 11)
-    return Fraction(u) < Fraction(pi) * 2 ** 53
+
+def exact_keep(pi: float, w: int) -> bool:
+    return Fraction(w) < Fraction(pi) * 2 ** 32
 
 
 @pytest.fixture(scope="module")
@@ -35,36 +35,60 @@ def harness(tmp_path_factory):
     assert r.returncode == 0, r.stderr
 
     def run(cases):
-        text = "".join(f"{struct.unpack('<Q', struct.pack('<d', pi * 4294967296.0))[0]:x} {w0} {w1}\n"
-                       for pi, w0, w1 in cases)
+        text = "".join(f"{struct.unpack('<Q', struct.pack('<d', pi * 4294967296.0))[0]:x} {w}\n"
+                       for pi, w in cases)
         out = subprocess.run([exe], input=text, capture_output=True, text=True, check=True)
         return [line == "1" for line in out.stdout.split()]
     return run
 
 
-def test_rule_matches_exact_compare(harness):
+def draw_cases():
     rng = np.random.default_rng(7)
     pis = [0.0, 1.0, 2.0 ** -32, 2.0 ** -33, 3 * 2.0 ** -34, 0.5, 0.1, 1 - 2.0 ** -33,
            1 - 2.0 ** -32, 1 - 2.0 ** -40, float(np.nextafter(1.0, 0.0)),
-           (2 ** 32 - 1) / 2 ** 32, 12345 / 2 ** 32, 12345.5 / 2 ** 32]
+           (2 ** 32 - 1) / 2 ** 32, 12345 / 2 ** 32, 12345.5 / 2 ** 32,
+           float(np.nextafter(12345 / 2 ** 32, 1.0)), float(np.nextafter(12345 / 2 ** 32, 0.0))]
     pis += [float(p) for p in rng.random(300)]
     pis += [float(p) for p in np.exp(rng.uniform(np.log(1e-12), 0.0, 200))]
     cases = []
     for pi in pis:
-        f = int(pi * 2 ** 32) if pi < 1 else 0xFFFFFFFF
-        w0s = {0, 0xFFFFFFFF, f, max(f - 1, 0), min(f + 1, 0xFFFFFFFF)}
-        w0s |= set(int(v) for v in rng.integers(0, 2 ** 32, 4))
-        for w0 in w0s:
-            # low words around the tie's split point and at the ends
-            x = Fraction(pi) * 2 ** 53 - (w0 << 21)
-            mid = int(x) << 11 if 0 <= x < 2 ** 21 else 0
-            for w1 in {0, 0xFFFFFFFF, mid, max(mid - 2048, 0), min(mid + 2048, 0xFFFFFFFF),
-                       int(rng.integers(0, 2 ** 32))}:
-                cases.append((pi, w0, w1))
+        x = Fraction(pi) * 2 ** 32
+        f = int(x)                       # floor(pi * 2^32)
+        ws = {0, 1, 0xFFFFFFFE, 0xFFFFFFFF}
+        ws |= {min(max(f + d, 0), 0xFFFFFFFF) for d in (-2, -1, 0, 1, 2)}
+        ws |= set(int(v) for v in rng.integers(0, 2 ** 32, 6))
+        cases += [(pi, w) for w in sorted(ws)]
+    return cases
+
+
+def test_rule_matches_exact_compare(harness):
+    cases = draw_cases()
     got = harness(cases)
     assert len(got) == len(cases) > 5000
-    ties = 0
-    for (pi, w0, w1), g in zip(cases, got):
-        assert g == exact_keep(pi, w0, w1), (pi, w0, w1)
-        ties += w0 == (int(pi * 2 ** 32) if pi < 1 else 0xFFFFFFFF)
-    assert ties > 1000          # the tie branch is exercised
+    boundary = 0
+    for (pi, w), g in zip(cases, got):
+        assert g == exact_keep(pi, w), (pi, w)
+        boundary += abs(Fraction(pi) * 2 ** 32 - w) <= 1
+    assert boundary > 1000            # cases on and next to the threshold
+
+
+def test_rule_extremes(harness):
+    # pi = 0 keeps nothing, pi = 1 keeps every word, pi = 2^-32 keeps w = 0 only
+    cases = [(0.0, 0), (0.0, 0xFFFFFFFF), (1.0, 0), (1.0, 0xFFFFFFFF),
+             (2.0 ** -32, 0), (2.0 ** -32, 1), (1 - 2.0 ** -32, 0xFFFFFFFE),
+             (1 - 2.0 ** -32, 0xFFFFFFFF)]
+    assert harness(cases) == [False, False, True, True, True, False, True, False]
+
+
+def test_oracle_rule_is_the_same_compare():
+    # sample_row keeps block j iff its word is below pi * 2^32: with scores
+    # that make every pi equal, the kept set is exactly the words below it
+    n, budget = 64, 0.25
+    s = np.full(n, 1.0, dtype=np.float32)
+    pi = oracle.inclusion_probabilities(s, budget)
+    assert np.all(pi == 0.25)
+    for seed in range(20):
+        cols, _ = oracle.sample_row(s, budget, 1, 2, 3, seed)
+        w = oracle.block_words(1, 2, 3, n, seed)
+        want = [j for j in range(n) if exact_keep(0.25, int(w[j]))]
+        assert cols.tolist() == want
