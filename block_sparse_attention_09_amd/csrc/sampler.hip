@@ -186,7 +186,11 @@ __device__ PiSolve solve_pi(const float* s, int n, double budget, RowStats st, R
 
 // Stage the row in LDS (or read it in place when it does not fit) and gather
 // the first-round statistics on the way: 16-byte loads when the row starts
-// 16-byte aligned, 4-byte loads otherwise.
+// 16-byte aligned, 4-byte loads otherwise.  Each thread issues kStageU loads
+// before it uses the first, so a row costs a few memory round trips rather
+// than one per load; the statistics still see the values in index order.
+constexpr int kStageU = 10;
+
 template <bool kLds>
 __device__ __forceinline__ const float* stage_row(const float* g, int n, float* lds,
                                                   RowStats& st) {
@@ -194,20 +198,42 @@ __device__ __forceinline__ const float* stage_row(const float* g, int n, float* 
   if ((reinterpret_cast<uintptr_t>(g) & 15) == 0) {
     const int n4 = n >> 2;
     const f32x4* g4 = reinterpret_cast<const f32x4*>(g);
-    for (int q = threadIdx.x; q < n4; q += kSampT) {
-      const f32x4 v = g4[q];
-      if constexpr (kLds) reinterpret_cast<f32x4*>(lds)[q] = v;
-      st.add(v[0]);
-      st.add(v[1]);
-      st.add(v[2]);
-      st.add(v[3]);
+    for (int q0 = threadIdx.x; q0 < n4; q0 += kStageU * kSampT) {
+      f32x4 v[kStageU];
+#pragma unroll
+      for (int u = 0; u < kStageU; ++u) {
+        const int q = q0 + u * kSampT;
+        if (q < n4) v[u] = g4[q];
+      }
+#pragma unroll
+      for (int u = 0; u < kStageU; ++u) {
+        const int q = q0 + u * kSampT;
+        if (q < n4) {
+          if constexpr (kLds) reinterpret_cast<f32x4*>(lds)[q] = v[u];
+          st.add(v[u][0]);
+          st.add(v[u][1]);
+          st.add(v[u][2]);
+          st.add(v[u][3]);
+        }
+      }
     }
     head = 4 * n4;
   }
-  for (int j = head + threadIdx.x; j < n; j += kSampT) {
-    const float v = g[j];
-    if constexpr (kLds) lds[j] = v;
-    st.add(v);
+  for (int j0 = head + threadIdx.x; j0 < n; j0 += kStageU * kSampT) {
+    float v[kStageU];
+#pragma unroll
+    for (int u = 0; u < kStageU; ++u) {
+      const int j = j0 + u * kSampT;
+      if (j < n) v[u] = g[j];
+    }
+#pragma unroll
+    for (int u = 0; u < kStageU; ++u) {
+      const int j = j0 + u * kSampT;
+      if (j < n) {
+        if constexpr (kLds) lds[j] = v[u];
+        st.add(v[u]);
+      }
+    }
   }
   if constexpr (kLds) {
     __syncthreads();
@@ -315,6 +341,8 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ count
   }
 }
 
+constexpr int kFillU = 4;
+
 __global__ __launch_bounds__(kSampT) void k_sip_fill(const float* __restrict__ S, int n,
                                                     int n_forced,
                                                     const uint32_t* __restrict__ masks,
@@ -363,13 +391,27 @@ __global__ __launch_bounds__(kSampT) void k_sip_fill(const float* __restrict__ S
       list[pos++] = (uint16_t)(32 * t + bit);
     }
     __syncthreads();
-    // every thread takes kept blocks i, i + kSampT, ...: coalesced writes
+    // every thread takes kept blocks i, i + kSampT, ...: coalesced writes;
+    // the scores of kFillU of them are requested before the first is used
     const int64_t out = start + run;
-    for (int i = t; i < tot; i += kSampT) {
-      const int j = 32 * base + list[i];
-      const double pi = pi_of(srow[j], ps);
-      col_idx[out + i] = j;
-      logw[out + i] = pi == 1.0 ? 0.0f : (float)(-log(pi));
+    for (int i0 = t; i0 < tot; i0 += kFillU * kSampT) {
+      int jj[kFillU];
+      float sv[kFillU];
+#pragma unroll
+      for (int u = 0; u < kFillU; ++u) {
+        const int i = i0 + u * kSampT;
+        jj[u] = i < tot ? 32 * base + list[i] : 0;
+        if (i < tot) sv[u] = srow[jj[u]];
+      }
+#pragma unroll
+      for (int u = 0; u < kFillU; ++u) {
+        const int i = i0 + u * kSampT;
+        if (i < tot) {
+          const double pi = pi_of(sv[u], ps);
+          col_idx[out + i] = jj[u];
+          logw[out + i] = pi == 1.0 ? 0.0f : (float)(-log(pi));
+        }
+      }
     }
     run += tot;
     __syncthreads();
