@@ -15,6 +15,8 @@ the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload wan14b_720p] [--budget 0.10]
     python bench.py --probe copy     # plain device copy, for counter calibration
+    python bench.py --record-traffic DIR   # write the attention kernel's HBM traffic record
+                                           # from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
 """
 from __future__ import annotations
 
@@ -121,6 +123,82 @@ def probe_copy(torch, steps: int):
                       "GB/s": 2 * n / ms / 1e6}))
 
 
+ATTEND_KERNEL = "abatt::k_attend_bf16<128, true, true>"
+TRAFFIC_COMMANDS = [
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o fetch -- "
+    "python3 -u bench.py --steps 2 --warmup 1 --no-cpu --no-dense",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o write -- "
+    "python3 -u bench.py --steps 2 --warmup 1 --no-cpu --no-dense",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/copyf -o copyf -- "
+    "python3 -u bench.py --probe copy --steps 3",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/copyw -o copyw -- "
+    "python3 -u bench.py --probe copy --steps 3",
+]
+
+
+def counter_dispatches(path: str, counter: str) -> dict:
+    """Kernel name -> per-dispatch totals of the counter (summed over its
+    instances), from the rocprofv3 counter_collection CSVs under `path`."""
+    import csv
+    import glob
+    from collections import defaultdict
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    per = defaultdict(lambda: defaultdict(float))
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                name = r["Kernel_Name"]
+                name = name[5:] if name.startswith("void ") else name
+                per[name.split("(")[0]][(f, r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def counter_means(path: str, counter: str) -> dict:
+    """Kernel name -> (mean over dispatches, dispatch count)."""
+    return {k: (sum(v) / len(v), len(v)) for k, v in counter_dispatches(path, counter).items()}
+
+
+def record_traffic(d: str, workload: str = "wan14b_720p", budget: float = 0.10) -> dict:
+    """HBM bytes per launch of the gathered attention kernel: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for the 1 GiB device copy of `--probe copy`; written to TRAFFIC_FILE with
+    the attention source's hash, so that bench.py reports it only while that
+    source is unchanged."""
+    n = 1 << 30
+    # the 1 GiB copy is the largest copy dispatch of each run
+    cf = [x for k, v in counter_dispatches(os.path.join(d, "copyf"), "FETCH_SIZE").items()
+          if "copyBuffer" in k for x in v]
+    cw = [x for k, v in counter_dispatches(os.path.join(d, "copyw"), "WRITE_SIZE").items()
+          if "copyBuffer" in k for x in v]
+    if not cf or not cw:
+        raise SystemExit("the copy runs hold no copyBuffer dispatch")
+    fetch_copy, write_copy = max(cf), max(cw)
+    fs, ws_ = n / (fetch_copy * 1024), n / (write_copy * 1024)
+    fe = counter_means(os.path.join(d, "fetch"), "FETCH_SIZE")
+    wr = counter_means(os.path.join(d, "write"), "WRITE_SIZE")
+    if ATTEND_KERNEL not in fe or ATTEND_KERNEL not in wr:
+        raise SystemExit(f"no {ATTEND_KERNEL} dispatch in the counter runs")
+    rec = {
+        "kernel": ATTEND_KERNEL,
+        "workload": workload,
+        "budget": budget,
+        "attend_src_sha": src_sha(os.path.join(ROOT, "block_sparse_attention_09_amd", "csrc",
+                                               "attend.hip")),
+        "fetch_kib_per_launch": fe[ATTEND_KERNEL][0],
+        "write_kib_per_launch": wr[ATTEND_KERNEL][0],
+        "copy_calibration": {"bytes_copied": n, "fetch_kib": fetch_copy, "write_kib": write_copy,
+                             "fetch_scale": fs, "write_scale": ws_},
+        "bytes_per_launch": (fe[ATTEND_KERNEL][0] * fs + wr[ATTEND_KERNEL][0] * ws_) * 1024,
+        "commands": [c.replace("DIR", d) for c in TRAFFIC_COMMANDS],
+        "other_kernels_kib_per_launch": {
+            k: {"fetch": fe[k][0], "write": wr.get(k, (0.0, 0))[0]} for k in fe
+            if k != ATTEND_KERNEL},
+    }
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,7 +217,18 @@ def main():
     ap.add_argument("--grid", default=None,
                     help="T,H,W latent grid in place of the workload's (block-size sweep)")
     ap.add_argument("--probe", choices=["copy"], default=None)
+    ap.add_argument("--record-traffic", default=None, metavar="DIR",
+                    help="write the attention traffic record from the counter runs under DIR "
+                         "(fetch/, write/, copyf/, copyw/) and exit; needs no GPU")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        rec = record_traffic(args.record_traffic)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(f"{TRAFFIC_FILE}: {rec['bytes_per_launch'] / 1e9:.2f} GB per launch")
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

@@ -25,8 +25,10 @@
 //     then stored row-major.  K and V of a group come from one row
 //     computation, and at D=128 the group's row base is wave-uniform and
 //     rides in the loads' scalar offset, so the gather costs few vector
-//     instructions (vector issue is the kernel's limit: an MFMA holds it for
-//     about half its duration).  The PV operand is read with the gfx950 LDS
+//     instructions (about 160 per chunk and wave beside 32 MFMAs: at that
+//     ratio they co-issue with the MFMAs of the other wave on the SIMD; what
+//     holds the matrix cores back is the dependency chain QK^T -> softmax ->
+//     PV inside each wave).  The PV operand is read with the gfx950 LDS
 //     transpose read, so PV runs as O^T = V^T P^T on fp16 MFMA with the
 //     probabilities straight from the softmax registers: the key order inside
 //     an MFMA k-step is chosen to match what each lane already holds;
