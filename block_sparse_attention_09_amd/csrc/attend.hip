@@ -14,9 +14,10 @@
 //     B operand of S^T = K Q^T (bf16 MFMA 32x32x16, fp32 accumulation), so a
 //     lane ends up holding 32 logits of ONE query (lane%32) and the row max
 //     needs a single exchange between the two half-waves;
-//   * keys arrive in chunks of 64 = 16 groups of 4 consecutive keys of the
-//     row's key sequence (one kept 4-token block per group; longer blocks
-//     span several groups).  A group of a head is 4*D*2 contiguous bytes, so
+//   * keys arrive in chunks of 4-key groups of the row's key sequence (one
+//     kept 4-token block per group; longer blocks span several groups): 32
+//     keys for gathered rows, so that three work-groups fit on a CU, and 64
+//     for dense rows.  A group of a head is 4*D*2 contiguous bytes, so
 //     one wave-wide 16-byte load moves a whole group (D=128).  The block ids
 //     of a chunk are fetched once per wave and broadcast with readlane.  K
 //     goes straight to LDS by direct buffer loads (gathered rows) into a tile
@@ -25,10 +26,10 @@
 //     then stored row-major.  K and V of a group come from one row
 //     computation, and at D=128 the group's row base is wave-uniform and
 //     rides in the loads' scalar offset, so the gather costs few vector
-//     instructions (about 160 per chunk and wave beside 32 MFMAs: at that
-//     ratio they co-issue with the MFMAs of the other wave on the SIMD; what
-//     holds the matrix cores back is the dependency chain QK^T -> softmax ->
-//     PV inside each wave).  The PV operand is read with the gfx950 LDS
+//     instructions (about 5 per MFMA: at that ratio they co-issue with the
+//     MFMAs of the other waves on the SIMD; what holds the matrix cores back
+//     is the dependency chain QK^T -> softmax -> PV inside each wave, which
+//     more waves per SIMD cover better).  The PV operand is read with the gfx950 LDS
 //     transpose read, so PV runs as O^T = V^T P^T on fp16 MFMA with the
 //     probabilities straight from the softmax registers: the key order inside
 //     an MFMA k-step is chosen to match what each lane already holds;
@@ -106,8 +107,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base
 
 // kV16: V arrives already converted to fp16.  Gathered rows move it to LDS
 // by direct loads like K; dense rows stage it through registers unconverted.
+// Gathered rows run in 32-key chunks, which keeps a work-group within 33 KB of
+// LDS and about 160 VGPRs, so three work-groups share a CU (three waves per
+// SIMD: measured 1.5-4% faster than two with 64-key chunks); dense rows run in
+// 64-key chunks, two work-groups per CU.
 template <int D, bool kGather, bool kV16>
-__global__ __launch_bounds__(256, 2) void k_attend_bf16(
+__global__ __launch_bounds__(256, kGather ? 3 : 2) void k_attend_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const float* __restrict__ logw, int64_t capacity,
@@ -116,17 +121,21 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   constexpr int KS = D / 16;          // QK^T k-steps
   constexpr int DT = D / 32;          // PV output tiles
   constexpr int CPR = D / 8;          // 16-byte chunks per row
-  constexpr int SLOTS = 2 * D / 64;   // 16-byte loads per lane per chunk, for K and for V
-  constexpr int BPS = 64 / (4 * CPR); // 4-key groups covered by one wave-wide load (1 or 2)
+  constexpr int CK = kGather ? 32 : 64;  // keys per chunk
+  constexpr int NG = CK / 4;             // 4-key groups per chunk
+  constexpr int TT = CK / 32;            // 32-key tiles per chunk
+  constexpr int WG = NG / 4;             // groups each wave moves per chunk
+  constexpr int BPS = 64 / (4 * CPR);    // 4-key groups covered by one wave-wide load (1 or 2)
+  constexpr int SLOTS = WG / BPS;        // 16-byte loads per lane per chunk, for K and for V
   constexpr int GROUP_BYTES = 4 * D * 2;  // one group of 4 keys
-  static_assert(SLOTS * BPS == 4, "a wave moves 4 groups of each chunk");
+  static_assert(SLOTS * BPS == WG && SLOTS >= 1, "a wave moves whole loads of each chunk");
   // K tile: row-major, 16-byte slot s of row r stored at s ^ (r % CPR)
   // (conflict-free operand reads without padding; the direct loads place each
   // lane's 16 bytes at a fixed LDS position, so the swizzle is chosen through
   // the source address)
-  __shared__ __align__(16) uint16_t Ks[2][64 * D];
-  __shared__ __align__(16) uint16_t Vs[2][64 * D];
-  __shared__ float lwb[2][16];
+  __shared__ __align__(16) uint16_t Ks[2][CK * D];
+  __shared__ __align__(16) uint16_t Vs[2][CK * D];
+  __shared__ float lwb[2][NG];
 
   // Plan rows in launch order: the dispatcher deals consecutive work-groups to
   // the 8 XCDs in turn, so all XCDs work on the same head at once and that
@@ -150,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     nblk = (N + 3) / 4;
   }
   // keys of the row: nblk blocks of 2^lkb tokens (dense rows: 4-token groups)
-  const int nchunk = (int)((((int64_t)nblk << lkb) + 63) / 64);
+  const int nchunk = (int)((((int64_t)nblk << lkb) + CK - 1) / CK);
   const int kbmask = (1 << lkb) - 1;
 
   const __amdgpu_buffer_rsrc_t krs = head_rsrc(K + bh * N * D, N * D * 2);
@@ -166,12 +175,12 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
       qreg[s] = bf16x8{};
   }
 
-  // A chunk is 64 consecutive keys of the row's key sequence, 16 groups of 4;
-  // group g of chunk c starts at key 64c + 4g, in block (64c + 4g) >> lkb at
-  // token (64c + 4g) & kbmask of the block.  Lane j holds the block id and
+  // A chunk is CK consecutive keys of the row's key sequence, NG groups of 4;
+  // group g of chunk c starts at key CK*c + 4g, in block (CK*c + 4g) >> lkb at
+  // token (CK*c + 4g) & kbmask of the block.  Lane j holds the block id and
   // shift of group j & 15 (repeated for blocks longer than 4), branch-free.
-  auto group_block = [&](int c, int g) { return (64 * c + 4 * g) >> lkb; };
-  auto group_token = [&](int c, int g) { return (64 * c + 4 * g) & kbmask; };
+  auto group_block = [&](int c, int g) { return (CK * c + 4 * g) >> lkb; };
+  auto group_token = [&](int c, int g) { return (CK * c + 4 * g) & kbmask; };
   // The row's ids and shifts are read through bounds-checked buffers: entries
   // past the row read zero, and valid_id rejects them by position.
   const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
@@ -179,13 +188,13 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(logw + start), (short)0, nblk * 4, 0x00020000);
   auto fetch_ids = [&](int c, int& id, float& lw) {
-    const int idx = group_block(c, lane & 15) * 4;
+    const int idx = group_block(c, lane & (NG - 1)) * 4;
     id = (int)__builtin_amdgcn_raw_buffer_load_b32(crs, idx, 0, 0);
     lw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lrs, idx, 0, 0));
   };
   // validity is applied when the ids are first used (keeps the loads in flight)
   auto valid_id = [&](int c, int raw) -> bool {
-    return group_block(c, lane & 15) < nblk && raw >= 0 && raw < n_kb;
+    return group_block(c, lane & (NG - 1)) < nblk && raw >= 0 && raw < n_kb;
   };
 
   // lane -> (group within a load, key within the group, 16-byte chunk); one
@@ -222,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   auto issue_kv = [&](int c, int idv, int stage) {
 #pragma unroll
     for (int j = 0; j < SLOTS; ++j) {
-      const int b0 = 4 * wv + BPS * j;
+      const int b0 = WG * wv + BPS * j;
       const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(
           &Ks[stage][b0 * (GROUP_BYTES / 2)]);
       if constexpr (BPS == 1) {
@@ -251,7 +260,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   // shifts in stage `stage` and issue its K and V.
   auto start_chunk = [&](int c, int stage) {
     const bool ok = valid_id(c, id_next);
-    if (t < 16) lwb[stage][t] = ok ? lw_next * kLog2e : -INFINITY;
+    if (t < NG) lwb[stage][t] = ok ? lw_next * kLog2e : -INFINITY;
     issue_kv(c, ok ? id_next : 0, stage);
   };
   // Dense rows: K and V of chunk c (keys 64c..64c+63) into registers.  The
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
   auto issue_dense = [&](int c) {
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
-      const int voff = (64 * c + 4 * (4 * wv + i * BPS + sub)) * ROW_BYTES + vlane;
+      const int voff = (CK * c + 4 * (WG * wv + i * BPS + sub)) * ROW_BYTES + vlane;
       kpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff, 0, 0));
       vpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, 0, 0));
     }
@@ -272,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     uint16_t* vst = Vs[buf];
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
-      const int row = 4 * (4 * wv + i * BPS + sub) + key;
+      const int row = 4 * (WG * wv + i * BPS + sub) + key;
       if constexpr (!kGather)
         *reinterpret_cast<u32x4*>(&Ks[buf][row * D + 8 * (dc ^ (row % CPR))]) = kpre[i];
       u32x4 hv;
@@ -336,11 +345,13 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     }
 
     // S^T tile: lane holds query l32, keys 32*tt + 8*g + 4*hh + (0..3) = group 8tt+2g+hh
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    f32x16 sacc[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) sacc[tt] = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int tt = 0; tt < TT; ++tt) {
         const int krow = 32 * tt + l32;
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(
             &kst[krow * D + (((2 * s + hh) ^ (krow % CPR)) << 3)]);
@@ -350,25 +361,25 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     // keep four K operand reads in flight ahead of the MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * KS - 4; ++i) {
+    for (int i = 0; i < TT * KS - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     if constexpr (!kGather) {
       if (c == nchunk - 1) {  // keys past N in the last dense chunk
-        const int base = 64 * c;
+        const int base = CK * c;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             if (base + 32 * tt + 8 * (v >> 2) + 4 * hh + (v & 3) >= N) sacc[tt][v] = -INFINITY;
       }
     }
-    float lwg[8];
+    float lwg[4 * TT];
     float mloc = -INFINITY;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < TT; ++tt) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         lwg[4 * tt + g] = kGather ? lwb[buf][8 * tt + 2 * g + hh] : 0.f;
@@ -389,9 +400,9 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
       for (int u = 0; u < DT; ++u) oacc[u] *= alpha;
     }
     const float mref = m_used == -INFINITY ? 0.f : m_used;
-    uint32_t pk[16];
+    uint32_t pk[8 * TT];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < TT; ++tt) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float sh = lwg[4 * tt + g] - mref;
@@ -409,7 +420,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     // O^T += V^T P^T.  k-step (tt, gp) covers keys 32tt+16gp .. +15 in the order
     // lane-half hh holds them: 4hh+{0..3}, then 8+4hh+{0..3}.
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < TT; ++tt) {
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
         const int pb = 8 * tt + 4 * gp;
@@ -436,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_bf16(
     if constexpr (kGather) {
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int i = 0; i < 2 * 2 * DT - 2; ++i) {
+      for (int i = 0; i < TT * 2 * DT - 2; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
