@@ -14,14 +14,15 @@
 //     B operand of S^T = K Q^T (bf16 MFMA 32x32x16, fp32 accumulation), so a
 //     lane ends up holding 32 logits of ONE query (lane%32) and the row max
 //     needs a single exchange between the two half-waves;
-//   * keys arrive in chunks of 4-key groups of the row's key sequence (one
-//     kept 4-token block per group; longer blocks span several groups): 32
-//     keys for gathered rows, so that three work-groups fit on a CU, and 64
-//     for dense rows.  A group of a head is 4*D*2 contiguous bytes, so
-//     one wave-wide 16-byte load moves a whole group (D=128).  The block ids
+//   * keys arrive in chunks of 32 = 8 groups of 4 consecutive keys of the
+//     row's key sequence (one kept 4-token block per group; longer blocks
+//     span several groups; dense rows take every group in order), small
+//     enough that three work-groups fit on a CU.  A group of a head is
+//     4*D*2 contiguous bytes, so one wave-wide 16-byte load moves a whole
+//     group (D=128).  The block ids
 //     of a chunk are fetched once per wave and broadcast with readlane.  K
-//     goes straight to LDS by direct buffer loads (gathered rows) into a tile
-//     with an XOR slot swizzle; V is loaded into registers and converted to
+//     goes straight to LDS by direct buffer loads into a tile with an XOR
+//     slot swizzle; V is loaded into registers and converted to
 //     fp16 while it is staged (exact for bf16 values in fp16's normal range),
 //     then stored row-major.  K and V of a group come from one row
 //     computation, and at D=128 the group's row base is wave-uniform and
@@ -105,14 +106,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base
                                            0x00020000);
 }
 
-// kV16: V arrives already converted to fp16.  Gathered rows move it to LDS
-// by direct loads like K; dense rows stage it through registers unconverted.
-// Gathered rows run in 32-key chunks, which keeps a work-group within 33 KB of
+// kV16: V arrives already converted to fp16 and moves to LDS by direct loads
+// like K.  Rows run in 32-key chunks, which keeps a work-group within 33 KB of
 // LDS and about 160 VGPRs, so three work-groups share a CU (three waves per
-// SIMD: measured 1.5-4% faster than two with 64-key chunks); dense rows run in
-// 64-key chunks, two work-groups per CU.
+// SIMD: measured 1.5-4% faster than two with 64-key chunks on gathered rows,
+// 6% on dense ones).
 template <int D, bool kGather, bool kV16>
-__global__ __launch_bounds__(256, kGather ? 3 : 2) void k_attend_bf16(
+__global__ __launch_bounds__(256, 3) void k_attend_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const float* __restrict__ logw, int64_t capacity,
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256, kGather ? 3 : 2) void k_attend_bf16(
   constexpr int KS = D / 16;          // QK^T k-steps
   constexpr int DT = D / 32;          // PV output tiles
   constexpr int CPR = D / 8;          // 16-byte chunks per row
-  constexpr int CK = kGather ? 32 : 64;  // keys per chunk
+  constexpr int CK = 32;                 // keys per chunk
   constexpr int NG = CK / 4;             // 4-key groups per chunk
   constexpr int TT = CK / 32;            // 32-key tiles per chunk
   constexpr int WG = NG / 4;             // groups each wave moves per chunk
@@ -216,25 +216,26 @@ __global__ __launch_bounds__(256, kGather ? 3 : 2) void k_attend_bf16(
         &Vs[stage][g * (GROUP_BYTES / 2)]);
   };
 
-  // Gathered rows: K goes straight to LDS, V through registers (converted to
-  // fp16 on its way to LDS).  Dense rows stage K through registers too
-  // (measured faster there).
-  u32x4 vpre[kGather && kV16 ? 1 : SLOTS], kpre[kGather ? 1 : SLOTS];
+  // K goes straight to LDS by direct loads; V too when it arrives as fp16,
+  // otherwise through registers (converted to fp16 on its way to LDS).
+  u32x4 vpre[kV16 ? 1 : SLOTS];
   int id_next = 0;                   // raw ids of the next chunk to start (gathered rows)
   float lw_next = 0.f;
 
-  // Gathered rows: K of chunk c into K stage `stage` (one direct load per
-  // 1 KB) and V of chunk c into registers, both from one row computation per
-  // group.  The ids `idv` are validated, so every row lies inside the head:
-  // when a load covers one group (D = 128) the group's row base is
-  // wave-uniform and goes in the scalar offset.
+  // K and V of chunk c into stage `stage`, from one row computation per group.
+  // Gathered rows: the ids `idv` are validated, so every row lies inside the
+  // head; when a load covers one group (D = 128) the group's row base is
+  // wave-uniform and goes in the scalar offset.  Dense rows: group g of chunk
+  // c is keys CK*c + 4g .. +3; rows past N (a partial last group, or whole
+  // groups of the last chunk) are clamped to row N-1, and their logits are
+  // masked.
   auto issue_kv = [&](int c, int idv, int stage) {
 #pragma unroll
     for (int j = 0; j < SLOTS; ++j) {
       const int b0 = WG * wv + BPS * j;
       const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(
           &Ks[stage][b0 * (GROUP_BYTES / 2)]);
-      if constexpr (BPS == 1) {
+      if constexpr (kGather && BPS == 1) {
         const int soff = __builtin_amdgcn_readfirstlane(
             ((__builtin_amdgcn_readlane(idv, b0) << lkb) + group_token(c, b0)) * ROW_BYTES);
         buffer_load_lds16(krs, klane(b0), soff, lds);
@@ -244,9 +245,16 @@ __global__ __launch_bounds__(256, kGather ? 3 : 2) void k_attend_bf16(
           vpre[j] = __builtin_bit_cast(
               u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vlane, soff, 0));
       } else {
-        const int r0 = (__builtin_amdgcn_readlane(idv, b0) << lkb) + group_token(c, b0);
-        const int r1 = (__builtin_amdgcn_readlane(idv, b0 + 1) << lkb) + group_token(c, b0 + 1);
-        const int rowoff = (sub ? r1 : r0) * ROW_BYTES;
+        int rowoff;
+        if constexpr (kGather) {
+          const int r0 = (__builtin_amdgcn_readlane(idv, b0) << lkb) + group_token(c, b0);
+          const int r1 = (__builtin_amdgcn_readlane(idv, b0 + 1) << lkb) + group_token(c, b0 + 1);
+          rowoff = (sub ? r1 : r0) * ROW_BYTES;
+        } else {
+          // this lane's key row, clamped; key * ROW_BYTES is part of klane/vlane
+          const int row = CK * c + 4 * (b0 + sub) + key;
+          rowoff = ((row < N ? row : N - 1) - key) * ROW_BYTES;
+        }
         buffer_load_lds16(krs, rowoff + klane(b0 + sub), 0, lds);
         if constexpr (kV16)
           buffer_load_lds16(vrs, rowoff + vlane_t(b0 + sub), 0, vlds(stage, b0));
@@ -256,43 +264,29 @@ __global__ __launch_bounds__(256, kGather ? 3 : 2) void k_attend_bf16(
       }
     }
   };
-  // Gathered rows: validate the ids of chunk c (in id_next) once, record its
-  // shifts in stage `stage` and issue its K and V.
+  // Chunk c into stage `stage`; gathered rows first validate the ids of the
+  // chunk (in id_next) once and record its shifts.
   auto start_chunk = [&](int c, int stage) {
-    const bool ok = valid_id(c, id_next);
-    if (t < NG) lwb[stage][t] = ok ? lw_next * kLog2e : -INFINITY;
-    issue_kv(c, ok ? id_next : 0, stage);
-  };
-  // Dense rows: K and V of chunk c (keys 64c..64c+63) into registers.  The
-  // whole row offset goes in the per-lane offset, which the buffer range
-  // check covers: rows past N (the last partial group) read zero.
-  auto issue_dense = [&](int c) {
-#pragma unroll
-    for (int i = 0; i < SLOTS; ++i) {
-      const int voff = (CK * c + 4 * (WG * wv + i * BPS + sub)) * ROW_BYTES + vlane;
-      kpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff, 0, 0));
-      vpre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, 0, 0));
+    if constexpr (kGather) {
+      const bool ok = valid_id(c, id_next);
+      if (t < NG) lwb[stage][t] = ok ? lw_next * kLog2e : -INFINITY;
+      issue_kv(c, ok ? id_next : 0, stage);
+    } else {
+      issue_kv(c, 0, stage);
     }
   };
-  // The chunk in registers into stage buf: V converted to fp16 (exact for
-  // bf16 values in fp16's normal range; as it is with fp16 V); dense rows: K
-  // as well.
+  // V of a chunk from registers into stage buf, converted to fp16 (exact for
+  // bf16 values in fp16's normal range; as it is with fp16 V).
   auto store_regs = [&](int buf) {
     uint16_t* vst = Vs[buf];
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
       const int row = 4 * (WG * wv + i * BPS + sub) + key;
-      if constexpr (!kGather)
-        *reinterpret_cast<u32x4*>(&Ks[buf][row * D + 8 * (dc ^ (row % CPR))]) = kpre[i];
       u32x4 hv;
-      if constexpr (kV16) {
-        hv = vpre[i];
-      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          hv[e] = pack_f16_rtz(__uint_as_float(vpre[i][e] << 16),
-                               __uint_as_float(vpre[i][e] & 0xffff0000u));
-      }
+      for (int e = 0; e < 4; ++e)
+        hv[e] = pack_f16_rtz(__uint_as_float(vpre[i][e] << 16),
+                             __uint_as_float(vpre[i][e] & 0xffff0000u));
       *reinterpret_cast<u32x4*>(&vst[row * D + 8 * (dc ^ vswz<D>(row))]) = hv;
     }
   };
@@ -305,27 +299,20 @@ __global__ __launch_bounds__(256, kGather ? 3 : 2) void k_attend_bf16(
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
   // Pipeline: chunk c is computed from LDS stage c%2; the other stage is free
-  // during iteration c.  Gathered rows: at the top of iteration c the ids of
-  // chunk c+1 (fetched during iteration c-1) are validated, K of chunk c+1
-  // goes to the free stage by direct loads and V of chunk c+1 to registers,
-  // and the ids of chunk c+2 are requested; after the chunk's PV the V
-  // registers are converted into the free stage.  Dense rows: chunk c+1 goes
-  // from the registers to the free stage and chunk c+2 is requested into the
-  // registers.  The barrier that ends iteration c waits for all of it, so
-  // every load has a whole iteration to land.  Chunk indices are clamped to
-  // the last chunk so the prefetch code runs unconditionally; the cost is a
-  // few redundant loads at the end.
+  // during iteration c.  At the top of iteration c, K of chunk c+1 goes to the
+  // free stage by direct loads and V of chunk c+1 to it as well (fp16 V) or to
+  // registers, converted into the free stage after the chunk's PV.  Gathered
+  // rows validate the ids of chunk c+1 (fetched during iteration c-1) first
+  // and request those of chunk c+2.  The barrier that ends iteration c waits
+  // for all of it, so every load has a whole iteration to land.  Chunk
+  // indices are clamped to the last chunk so the prefetch code runs
+  // unconditionally; the cost is a few redundant loads at the end.
   const int clast = nchunk > 0 ? nchunk - 1 : 0;
   if (nchunk > 0) {
-    if constexpr (kGather) {
-      fetch_ids(0, id_next, lw_next);
-      start_chunk(0, 0);
-      fetch_ids(min(1, clast), id_next, lw_next);
-    } else {
-      issue_dense(0);
-    }
-    if constexpr (!(kGather && kV16)) store_regs(0);
-    if constexpr (!kGather) issue_dense(min(1, clast));
+    if constexpr (kGather) fetch_ids(0, id_next, lw_next);
+    start_chunk(0, 0);
+    if constexpr (kGather) fetch_ids(min(1, clast), id_next, lw_next);
+    if constexpr (!kV16) store_regs(0);
   }
   dma_barrier();
 
@@ -336,13 +323,8 @@ __global__ __launch_bounds__(256, kGather ? 3 : 2) void k_attend_bf16(
   auto step = [&](int c, int buf) {
     const uint16_t* kst = Ks[buf];
     const uint16_t* vst = Vs[buf];
-    if constexpr (kGather) {
-      start_chunk(min(c + 1, clast), buf ^ 1);          // K, V of chunk c+1
-      fetch_ids(min(c + 2, clast), id_next, lw_next);   // ids of chunk c+2
-    } else {
-      store_regs(buf ^ 1);                // chunk c+1: registers -> free stage
-      issue_dense(min(c + 2, clast));     // chunk c+2 -> registers
-    }
+    start_chunk(min(c + 1, clast), buf ^ 1);                                // K, V of chunk c+1
+    if constexpr (kGather) fetch_ids(min(c + 2, clast), id_next, lw_next);  // ids of chunk c+2
 
     // S^T tile: lane holds query l32, keys 32*tt + 8*g + 4*hh + (0..3) = group 8tt+2g+hh
     f32x16 sacc[TT];
@@ -453,7 +435,7 @@ __global__ __launch_bounds__(256, kGather ? 3 : 2) void k_attend_bf16(
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    if constexpr (kGather && !kV16) store_regs(buf ^ 1);   // V of chunk c+1 -> free stage
+    if constexpr (!kV16) store_regs(buf ^ 1);   // V of chunk c+1 -> free stage
     dma_barrier();
   };
   if constexpr (kGather) {
