@@ -438,15 +438,11 @@ __global__ __launch_bounds__(256, 3) void k_attend_bf16(
     if constexpr (!kV16) store_regs(buf ^ 1);   // V of chunk c+1 -> free stage
     dma_barrier();
   };
-  if constexpr (kGather) {
-    // unrolled by two so that stage addresses are constants (measured faster
-    // for the gathered rows, slower for the dense ones)
-    for (int c = 0; c < nchunk; c += 2) {
-      step(c, 0);
-      if (c + 1 < nchunk) step(c + 1, 1);
-    }
-  } else {
-    for (int c = 0; c < nchunk; ++c) step(c, c & 1);
+  // unrolled by two so that stage addresses are constants (measured faster,
+  // gathered and dense rows alike)
+  for (int c = 0; c < nchunk; c += 2) {
+    step(c, 0);
+    if (c + 1 < nchunk) step(c + 1, 1);
   }
 
   // epilogue: O^T lane layout = query l32, dims 32u + 8g + 4hh + (0..3)
