@@ -341,14 +341,15 @@ def main():
         del scratch
         log(f"attend from a cold cache: median {attend_cold_ms:.3f} ms over {args.cold_reps} reps")
 
-    # per-row counts of the timed plan: computed tiles include the padding of
-    # each row's last 64-key chunk; useful work excludes the padded query rows
-    # of a head's last query block
+    # per-row counts of the timed plan: executed tiles include the padding of
+    # each row's last key chunk (32 keys in both the bf16 and the fp32 kernel);
+    # useful work excludes the padded query rows of a head's last query block
     kb = wl.kv_block
     rp = pl.row_ptr.cpu().numpy().astype(np.int64)
     row_nnz = np.diff(rp)
     valid_q = np.minimum(128, wl.N - 128 * (np.arange(prob.R) % prob.n_qb))
-    executed_keys = int((np.ceil(row_nnz * kb / 64.0) * 64).sum())
+    chunk = 32
+    executed_keys = int((np.ceil(row_nnz * kb / chunk) * chunk).sum())
     useful_flop = float((row_nnz * valid_q).sum()) * 4 * kb * wl.D
 
     # the library's dense attention, the speed-up denominator: for bf16 layers
