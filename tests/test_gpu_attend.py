@@ -65,9 +65,12 @@ def test_budget_one_equals_dense(name):
 
 
 @pytest.mark.parametrize("N,dtype,D", [(1000, "bf16", 128), (1030, "bf16", 64), (333, "f32", 64),
-                                       (129, "bf16", 128)])
+                                       (129, "bf16", 128), (1, "bf16", 128), (5, "bf16", 128),
+                                       (31, "bf16", 64), (33, "bf16", 128), (64, "bf16", 128),
+                                       (65, "bf16", 64)])
 def test_dense_ragged_lengths(N, dtype, D):
-    # dense accepts any N: the last key chunk and the last query block are partial
+    # dense accepts any N: the last key chunk (32 keys) and the last query block
+    # are partial; rows past N are clamped and masked, down to a single key
     rng = np.random.default_rng(N)
     shape = (1, 2, N, D)
     q, k, v = (rng.standard_normal(shape).astype(np.float32) for _ in range(3))
