@@ -11,10 +11,10 @@
 //   * pi: m = budget * n expected blocks; repeat c = (m - #certain) /
 //     sum(uncertain positive scores) and make every uncertain block with
 //     c*s >= 1 certain, until none is added (the first round's count, sum
-//     and maximum are gathered while the row is staged).  The certain set is always a top
-//     set of the scores, so it is held as a threshold theta (certain iff
-//     s >= theta).  float64 throughout; sums are fixed-order tree reductions,
-//     so every run gives the same bits.
+//     and maximum are gathered while the row is staged).  The certain set
+//     is always a top set of the scores, so it is held as a threshold theta
+//     (certain iff s >= theta).  float64 throughout; sums are fixed-order
+//     tree reductions, so every run gives the same bits.
 //   * draws: block j uses word j%4 of Philox4x32-10 with counter
 //     (j/4, qb, h, b) and key (seed low, seed high) as a 32-bit uniform
 //     integer w; kept iff w < pi_j * 2^32 (exact compare), so it enters with
