@@ -311,6 +311,17 @@ def main():
     torch.cuda.synchronize()
     plan_ms = s2.elapsed_time(e2) / args.steps
 
+    # the opt-in one-pass plan entry point (the same plan), for comparison
+    s3, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s3.record(stream)
+    for i in range(args.steps):
+        ab.plan_onepass(q, k, budget, seed=wl.plan_seed + i, problem=prob, ws=ws, out=pl)
+    e3.record(stream)
+    torch.cuda.synchronize()
+    plan_onepass_ms = s3.elapsed_time(e3) / args.steps
+    assert pl.ok(), "one-pass plan exceeded its capacity"
+    log(f"plan {plan_ms:.3f} ms, one-pass plan {plan_onepass_ms:.3f} ms")
+
     # the V conversion alone
     convert_ms = 0.0
     if v16 is not None:
@@ -427,6 +438,7 @@ def main():
             "attend_ms": attend_ms,
             "v_to_f16_ms": convert_ms,
             "plan_ms": plan_ms,
+            "plan_onepass_ms": plan_onepass_ms,
             "attend_plus_plan_over_4_ms": call_ms + plan_ms / 4,
             "dense_ms": dense_ms,
             "dense_onecall_ms": dense_onecall_ms,

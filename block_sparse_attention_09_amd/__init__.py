@@ -31,7 +31,7 @@ SCRATCH_BYTES = 256 * 1024 * 1024   # ABATT_SCRATCH_BYTES in abatt.h
 SYMBOLS = (
     "abatt_plan_rows", "abatt_plan_max_nnz", "abatt_plan_nnz_bound",
     "abatt_plan_workspace_bytes", "abatt_sampler_workspace_bytes", "abatt_plan",
-    "abatt_plan_noalloc", "abatt_attend", "abatt_v_to_f16", "abatt_attend_v16", "abatt_dense",
+    "abatt_plan_onepass", "abatt_plan_noalloc", "abatt_attend", "abatt_v_to_f16", "abatt_attend_v16", "abatt_dense",
     "abatt_dense_v16",
     "abatt_key_means", "abatt_scores", "abatt_plan_from_scores", "abatt_status_str",
     "abatt_version",
@@ -74,6 +74,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "abatt_sampler_workspace_bytes": (sz, [P]),
         "abatt_plan": (st, [P, vp, vp, ctypes.c_double, ctypes.c_uint64, vp, sz,
                             ctypes.POINTER(_Plan), vp]),
+        "abatt_plan_onepass": (st, [P, vp, vp, ctypes.c_double, ctypes.c_uint64, vp, sz,
+                                    ctypes.POINTER(_Plan), vp]),
         "abatt_plan_noalloc": (st, [P, vp, vp, ctypes.c_double, ctypes.c_uint64,
                                     ctypes.POINTER(_Plan), vp]),
         "abatt_attend": (st, [P, vp, vp, vp, ctypes.POINTER(_Plan), vp, vp, vp]),
@@ -268,6 +270,18 @@ def plan(q: torch.Tensor, k: torch.Tensor, budget: float, seed: int = 0,
          problem: Optional[Problem] = None, capacity: Optional[int] = None,
          ws: Optional[torch.Tensor] = None, out: Optional[Plan] = None) -> Plan:
     """IBCS + SIP on the GPU: returns a device CSR plan (abatt_plan)."""
+    return _plan_call("abatt_plan", q, k, budget, seed, problem, capacity, ws, out)
+
+
+def plan_onepass(q: torch.Tensor, k: torch.Tensor, budget: float, seed: int = 0,
+                 problem: Optional[Problem] = None, capacity: Optional[int] = None,
+                 ws: Optional[torch.Tensor] = None, out: Optional[Plan] = None) -> Plan:
+    """abatt_plan_onepass: the plan of plan(), bit for bit, with the sampler's
+    count, scan and fill done by one kernel (decoupled look-back)."""
+    return _plan_call("abatt_plan_onepass", q, k, budget, seed, problem, capacity, ws, out)
+
+
+def _plan_call(entry: str, q, k, budget, seed, problem, capacity, ws, out) -> Plan:
     prob = problem or Problem.like(q)
     _qkv_check(prob, q, k)
     lib = load_library()
@@ -282,9 +296,9 @@ def plan(q: torch.Tensor, k: torch.Tensor, budget: float, seed: int = 0,
             or ws.dtype != torch.uint8:
         raise ValueError(f"ws must be a contiguous uint8 tensor on {q.device}")
     cp = out.c()
-    _check(lib.abatt_plan(ctypes.byref(prob.c()), _ptr(q), _ptr(k), float(budget),
-                          ctypes.c_uint64(seed), _ptr(ws), ws.numel(), ctypes.byref(cp),
-                          _stream()))
+    _check(getattr(lib, entry)(ctypes.byref(prob.c()), _ptr(q), _ptr(k), float(budget),
+                               ctypes.c_uint64(seed), _ptr(ws), ws.numel(), ctypes.byref(cp),
+                               _stream()))
     return out
 
 

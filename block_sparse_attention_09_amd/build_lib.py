@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libabatt.so")
 
-SOURCES = ["key_means.hip", "kmeans.hip", "score.hip", "sampler.hip", "attend.hip", "scratch.hip",
+SOURCES = ["key_means.hip", "kmeans.hip", "score.hip", "sampler.hip", "sampler_onepass.hip", "attend.hip", "scratch.hip",
            "abatt.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

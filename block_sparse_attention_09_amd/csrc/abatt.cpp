@@ -83,6 +83,12 @@ struct PlanWs {
   size_t kmean, mu, w, S, sampler, total;
 };
 
+// the sampler's scratch, for either sampler
+size_t sampler_region(const Shape& s) {
+  const size_t a = abatt::sampler_ws_layout(s).total, b = abatt::onepass_ws_layout(s).total;
+  return a > b ? a : b;
+}
+
 PlanWs plan_ws_layout(const Shape& s) {
   PlanWs l;
   size_t off = 0;
@@ -95,12 +101,12 @@ PlanWs plan_ws_layout(const Shape& s) {
   l.S = off;
   off = align_up(off + (size_t)s.R * s.n_kbs * sizeof(float));
   l.sampler = off;
-  off = align_up(off + abatt::sampler_ws_layout(s).total);
+  off = align_up(off + sampler_region(s));
   l.total = off;
   return l;
 }
 
-size_t sampler_ws_bytes(const Shape& s) { return align_up(abatt::sampler_ws_layout(s).total); }
+size_t sampler_ws_bytes(const Shape& s) { return align_up(sampler_region(s)); }
 
 abatt_status hip_status(hipError_t e) { return e == hipSuccess ? ABATT_OK : ABATT_EHIP; }
 
@@ -124,16 +130,19 @@ hipError_t run_scores(const Shape& s, const PlanWs& l, char* ws, const void* Q, 
   return e;
 }
 
-// The whole plan (selector, then sampler) on the workspace `ws` laid out as l.
+// The whole plan (selector, then sampler) on the workspace `ws` laid out as l;
+// onepass selects the one-pass sampler (the same plan).
 hipError_t run_plan(const Shape& s, const PlanWs& l, char* ws, const void* Q, const void* K,
-                    double budget, uint64_t seed, const abatt_plan_t* plan, hipStream_t stream) {
+                    double budget, uint64_t seed, const abatt_plan_t* plan, hipStream_t stream,
+                    bool onepass = false) {
   float* mu = reinterpret_cast<float*>(ws + l.mu);
   float* w = reinterpret_cast<float*>(ws + l.w);
   float* S = reinterpret_cast<float*>(ws + l.S);
   hipError_t e = run_scores(s, l, ws, Q, K, mu, w, S, stream);
   if (e == hipSuccess)
-    e = abatt::launch_sampler(s, S, budget, seed, ws + l.sampler, plan->row_ptr, plan->col_idx,
-                              plan->logw, plan->capacity, plan->status, stream);
+    e = (onepass ? abatt::launch_sampler_onepass : abatt::launch_sampler)(
+        s, S, budget, seed, ws + l.sampler, plan->row_ptr, plan->col_idx, plan->logw,
+        plan->capacity, plan->status, stream);
   return e;
 }
 
@@ -239,6 +248,23 @@ abatt_status abatt_plan(const abatt_problem_t* p, const void* Q, const void* K, 
   if (plan->capacity < (int64_t)s.R * (s.n_kb - s.n_kbs)) return ABATT_ECAPACITY;
   return hip_status(run_plan(s, l, static_cast<char*>(workspace), Q, K, budget, seed, plan,
                              stream));
+}
+
+abatt_status abatt_plan_onepass(const abatt_problem_t* p, const void* Q, const void* K,
+                                double budget, uint64_t seed, void* workspace,
+                                size_t workspace_bytes, abatt_plan_t* plan, hipStream_t stream) {
+  Shape s;
+  abatt_status st = make_shape(p, &s);
+  if (st != ABATT_OK) return st;
+  if (bad(Q) || bad(K) || bad(workspace) || !budget_ok(budget))
+    return ABATT_EINVAL;
+  st = check_plan(s, plan, true);
+  if (st != ABATT_OK) return st;
+  const PlanWs l = plan_ws_layout(s);
+  if (workspace_bytes < l.total) return ABATT_EWORKSPACE;
+  if (plan->capacity < (int64_t)s.R * (s.n_kb - s.n_kbs)) return ABATT_ECAPACITY;
+  return hip_status(run_plan(s, l, static_cast<char*>(workspace), Q, K, budget, seed, plan,
+                             stream, true));
 }
 
 abatt_status abatt_plan_noalloc(const abatt_problem_t* p, const void* Q, const void* K,

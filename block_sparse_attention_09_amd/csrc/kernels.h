@@ -46,6 +46,17 @@ hipError_t launch_sampler(const Shape& s, const float* S, double budget, uint64_
                           void* ws, int32_t* row_ptr, int32_t* col_idx, float* logw,
                           int64_t capacity, int32_t* status, hipStream_t st);
 
+// sampler_onepass.hip: the same plan in one pass (decoupled look-back over
+// per-row records); its scratch (a ticket and one record per row) in `ws`.
+// Status 2 marks a plan whose look-back hit its spin bound.
+struct OnePassWs {
+  size_t ticket, flags, total;
+};
+OnePassWs onepass_ws_layout(const Shape& s);
+hipError_t launch_sampler_onepass(const Shape& s, const float* S, double budget, uint64_t seed,
+                                  void* ws, int32_t* row_ptr, int32_t* col_idx, float* logw,
+                                  int64_t capacity, int32_t* status, hipStream_t st);
+
 // attend.hip: gathered (plan != null) or dense attention; v16: V given as
 // fp16 (bf16 problems)
 hipError_t launch_attend(const Shape& s, const void* Q, const void* K, const void* V,

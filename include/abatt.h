@@ -161,6 +161,29 @@ abatt_status abatt_plan(const abatt_problem_t *p, const void *Q, const void *K,
                         hipStream_t stream);
 
 /*
+ * abatt_plan_onepass -- abatt_plan with the sampler fused into one pass (the
+ * fused-selector form that removes the second read of the score matrix).
+ * Same arguments, checks, workspace and results, bit for bit, as
+ * abatt_plan: the same scores, pi and draws.  One work-group per plan row,
+ * rows taken in ticket order, solves pi, draws, finds the row's offset in
+ * the plan from the counts of the rows before it (decoupled look-back over
+ * one 64-bit record per row) and writes the row from LDS, so no scan or fill
+ * launch follows and the score matrix is read once.  On MI355X it is slower
+ * than abatt_plan (the draw phase keeps its kept-block lists in LDS and runs
+ * at fewer waves per CU); it is kept for that comparison.
+ *   - The look-back waits only for rows that took their tickets earlier, so
+ *     it always ends; its spin is bounded all the same, and a plan whose
+ *     look-back hit the bound gets *status = 2 (invalid, like an overflow).
+ *   - On overflow (*status = 1) the rows that fit may have been written;
+ *     the plan is invalid as with abatt_plan.
+ *   - Concurrent calls need separate workspaces, as for abatt_plan.
+ */
+abatt_status abatt_plan_onepass(const abatt_problem_t *p, const void *Q, const void *K,
+                                double budget, uint64_t seed, void *workspace,
+                                size_t workspace_bytes, abatt_plan_t *plan,
+                                hipStream_t stream);
+
+/*
  * abatt_plan_noalloc -- abatt_plan for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Same arguments, checks and results (bit for bit) as

@@ -74,6 +74,36 @@ def test_bad_problems(lib, kw, code):
     assert r == code
 
 
+@pytest.mark.parametrize("entry", ["abatt_plan", "abatt_plan_onepass"])
+def test_plan_entries_check_alike(lib, entry):
+    # both planning entry points take the same arguments and reject the same
+    # ones with the same codes, before any HIP call
+    f = getattr(lib, entry)
+    P = ctypes.byref
+    fake = ctypes.c_void_p(0x1000)
+    good = ab._Plan(0x1000, 0x1000, 0x1000, 10 ** 6, 0x1000)
+    for kw, code in ((dict(D=96), -2), (dict(kv_block=256), -2), (dict(N=0), -1),
+                     (dict(n_forced_tail=6), -1), (dict(kmeans_iters=0), -1)):
+        assert f(P(prob(**kw).c()), fake, fake, 0.1, 0, fake, 1 << 40, P(good), None) == code
+    p = prob()
+    c = p.c()
+    ws = ab.plan_workspace_bytes(p)
+    assert f(P(c), None, fake, 0.1, 0, fake, ws, P(good), None) == -1
+    for b in (0.0, -0.1, 1.5, float("nan")):
+        assert f(P(c), fake, fake, b, 0, fake, ws, P(good), None) == -1
+    assert f(P(c), fake, fake, 0.1, 0, fake, ws - 1, P(good), None) == -3
+    assert f(P(c), fake, fake, 0.1, 0, None, ws, P(good), None) == -1
+    nostat = ab._Plan(0x1000, 0x1000, 0x1000, 10 ** 6, None)
+    assert f(P(c), fake, fake, 0.1, 0, fake, ws, P(nostat), None) == -1
+    pf = prob(N=1280, n_forced_tail=256).c()
+    small = ab._Plan(0x1000, 0x1000, 0x1000, 10, 0x1000)
+    assert f(P(pf), fake, fake, 0.1, 0, fake, lib.abatt_plan_workspace_bytes(P(pf)),
+             P(small), None) == -4
+    odd = ctypes.c_void_p(0x1008)
+    assert f(P(c), fake, odd, 0.1, 0, fake, ws, P(good), None) == -1
+    assert f(P(c), fake, fake, 0.1, 0, odd, ws, P(good), None) == -1
+
+
 @pytest.mark.parametrize("kb", [4, 8, 16, 32, 64, 128])
 def test_key_block_sizes(lib, kb):
     # powers of two from 4 to 128 tokens; blocks and forced blocks scale with kb

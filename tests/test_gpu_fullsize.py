@@ -128,6 +128,13 @@ def test_fullsize_plan_attend(name):
         assert abs(nnz - expect) < 6 * np.sqrt(op.R * m)
         check_plan_and_attend(f"{name} budget {budget}", wl, budget, wl.plan_seed, q2, k2, v2,
                               q, k, v, prob, op, pl, o)
+        # the one-pass sampler: the same plan, bit for bit
+        p1 = ab.plan_onepass(q, k, budget, seed=wl.plan_seed, problem=prob)
+        torch.cuda.synchronize()
+        assert p1.ok() and torch.equal(p1.row_ptr, pl.row_ptr)
+        assert torch.equal(p1.col_idx[:nnz], pl.col_idx[:nnz])
+        assert torch.equal(p1.logw[:nnz].view(torch.int32), pl.logw[:nnz].view(torch.int32))
+        del p1
         # the fp16-V form bench.py times: bit-identical to the attention just checked
         o16 = ab.attend(q, k, ab.v_to_f16(v, prob), pl, problem=prob)
         torch.cuda.synchronize()
