@@ -27,18 +27,21 @@
 //     then stored row-major.  K and V of a group come from one row
 //     computation, and at D=128 the group's row base is wave-uniform and
 //     rides in the loads' scalar offset, so the gather costs few vector
-//     instructions (about 5 per MFMA: at that ratio they co-issue with the
-//     MFMAs of the other waves on the SIMD; what holds the matrix cores back
-//     is the dependency chain QK^T -> softmax -> PV inside each wave, which
-//     more waves per SIMD cover better).  The PV operand is read with the gfx950 LDS
+//     instructions (about 4 per MFMA, exponentials included: at that ratio
+//     they co-issue with the MFMAs of the other waves on the SIMD; what holds
+//     the matrix cores back is the dependency chain QK^T -> softmax -> PV
+//     inside each wave, which more waves per SIMD cover better).  The PV operand is read with the gfx950 LDS
 //     transpose read, so PV runs as O^T = V^T P^T on fp16 MFMA with the
 //     probabilities straight from the softmax registers: the key order inside
 //     an MFMA k-step is chosen to match what each lane already holds;
 //   * two LDS stages: K and V of chunk c+1 arrive while chunk c is computed,
 //     one barrier per chunk;
-//   * online softmax in the exp2 domain; the running max is only moved when
-//     a chunk raises it by more than 8 (log2 units), so most chunks skip the
-//     rescale of the accumulators (p then stays below 2^8, fine for fp16);
+//   * online softmax in the exp2 domain against a reference that trails the
+//     running max: probabilities are formed against it first, and only when
+//     a half-chunk's fp16 sum passes 2^15 (a value may leave fp16's range)
+//     does the wave take the chunk's exact max, move the reference (when the
+//     max passes it by more than 8, log2 units), rescale the accumulators
+//     and form them again.  Most chunks take no max at all;
 //   * work-groups run in plan-row order, so all XCDs share one head at a time
 //     and its K/V stays resident in the Infinity Cache.
 // fp32 kernel: plain fp32 arithmetic (one thread per query), used for fp32
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(256, 3) void k_attend_bf16(
 #pragma unroll
   for (int u = 0; u < DT; ++u) oacc[u] = f32x16{};
   float m_used = -INFINITY;
-  float lsum0 = 0.f, lsum1 = 0.f;
+  float lsum = 0.f;
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
   // Pipeline: chunk c is computed from LDS stage c%2; the other stage is free
@@ -359,52 +362,74 @@ __global__ __launch_bounds__(256, 3) void k_attend_bf16(
       }
     }
     float lwg[4 * TT];
-    float mloc = -INFINITY;
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        lwg[4 * tt + g] = kGather ? lwb[buf][8 * tt + 2 * g + hh] : 0.f;
-        const float gm = fmaxf(fmaxf(sacc[tt][4 * g], sacc[tt][4 * g + 1]),
-                               fmaxf(sacc[tt][4 * g + 2], sacc[tt][4 * g + 3]));
-        mloc = fmaxf(mloc, fmaf(gm, scale_log2, lwg[4 * tt + g]));
-      }
-    }
-    const f32x2 mp = pair_x32(mloc);
-    const float mrow = fmaxf(mp[0], mp[1]);
-    const bool need = mrow > m_used + kRescaleLog2;
-    if (__any(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_used - mrow) : 1.f;
-      if (need) m_used = mrow;
-      lsum0 *= alpha;
-      lsum1 *= alpha;
-#pragma unroll
-      for (int u = 0; u < DT; ++u) oacc[u] *= alpha;
-    }
-    const float mref = m_used == -INFINITY ? 0.f : m_used;
+      for (int g = 0; g < 4; ++g) lwg[4 * tt + g] = kGather ? lwb[buf][8 * tt + 2 * g + hh] : 0.f;
     uint32_t pk[8 * TT];
+    // fp16 probabilities of half gp of tile tt (this lane's groups 2gp and
+    // 2gp+1) against the reference mr; returns their sum (the row sum takes
+    // the same fp16 values as the numerator)
+    auto probs = [&](int tt, int gp, float mr) -> float {
+      float cs = 0.f;
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float sh = lwg[4 * tt + g] - mref;
+      for (int g = 2 * gp; g < 2 * gp + 2; ++g) {
+        const float sh = lwg[4 * tt + g] - mr;
         float p[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           p[q] = __builtin_amdgcn_exp2f(fmaf(sacc[tt][4 * g + q], scale_log2, sh));
         pk[8 * tt + 2 * g] = pack_f16_rne(p[0], p[1]);
         pk[8 * tt + 2 * g + 1] = pack_f16_rne(p[2], p[3]);
-        // the row sum uses the same fp16 probabilities as the numerator
-        lsum0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[8 * tt + 2 * g]), ones, lsum0, false);
-        lsum1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[8 * tt + 2 * g + 1]), ones, lsum1, false);
+        cs = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[8 * tt + 2 * g]), ones, cs, false);
+        cs = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[8 * tt + 2 * g + 1]), ones, cs, false);
       }
-    }
-    // O^T += V^T P^T.  k-step (tt, gp) covers keys 32tt+16gp .. +15 in the order
-    // lane-half hh holds them: 4hh+{0..3}, then 8+4hh+{0..3}.
+      return cs;
+    };
+    // exact shifted maximum of the chunk; the reference moves to it when it
+    // passes the reference by more than kRescaleLog2, and the accumulators
+    // follow
+    auto rescale = [&]() {
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        // an opaque copy keeps this maximum on the rare path (the compiler
+        // would otherwise hoist part of it above the branch)
+        f32x16 sx = sacc[tt];
+        asm volatile("" : "+v"(sx));
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float gm = fmaxf(fmaxf(sx[4 * g], sx[4 * g + 1]), fmaxf(sx[4 * g + 2], sx[4 * g + 3]));
+          mloc = fmaxf(mloc, fmaf(gm, scale_log2, lwg[4 * tt + g]));
+        }
+      }
+      const f32x2 mp = pair_x32(mloc);
+      const float mrow = fmaxf(mp[0], mp[1]);
+      const bool need = mrow > m_used + kRescaleLog2;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_used - mrow) : 1.f;
+      if (need) m_used = mrow;
+      lsum *= alpha;
+#pragma unroll
+      for (int u = 0; u < DT; ++u) oacc[u] *= alpha;
+    };
+    // O^T += V^T P^T, one half-tile at a time.  k-step (tt, gp) covers keys
+    // 32tt+16gp .. +15 in the order lane-half hh holds them: 4hh+{0..3}, then
+    // 8+4hh+{0..3}.  Each half's probabilities are formed against the current
+    // reference first; if their sum passes 2^15 on any lane (so that a value
+    // may leave fp16's range; also inf or NaN while the reference is still
+    // -inf), the wave takes the exact maximum, moves the reference and forms
+    // them again.  Otherwise every value is at most 2^15, and the half goes
+    // straight to its MFMAs.
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
+        float cs = probs(tt, gp, m_used);
+        if (__builtin_expect(__any(__float_as_uint(cs) > 0x47000000u), 0)) {
+          rescale();
+          cs = probs(tt, gp, m_used == -INFINITY ? 0.f : m_used);
+        }
+        lsum += cs;
         const int pb = 8 * tt + 4 * gp;
         const f16x8 pop =
             __builtin_bit_cast(f16x8, u32x4{pk[pb], pk[pb + 1], pk[pb + 2], pk[pb + 3]});
@@ -422,19 +447,6 @@ __global__ __launch_bounds__(256, 3) void k_attend_bf16(
         }
       }
     }
-    // gathered rows: keep four transpose reads (two MFMAs' operands) in flight
-    // ahead of the PV MFMAs (measured: 1% faster than the compiler's own
-    // order; two, six or eight ahead are slower, and so is the dense kernel
-    // with it)
-    if constexpr (kGather) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < TT * 2 * DT - 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
     if constexpr (!kV16) store_regs(buf ^ 1);   // V of chunk c+1 -> free stage
     dma_barrier();
   };
@@ -446,7 +458,6 @@ __global__ __launch_bounds__(256, 3) void k_attend_bf16(
   }
 
   // epilogue: O^T lane layout = query l32, dims 32u + 8g + 4hh + (0..3)
-  const float lsum = lsum0 + lsum1;
   const f32x2 lp = pair_x32(lsum);
   const float ltot = lp[0] + lp[1];
   if (qrow < N) {
