@@ -9,7 +9,10 @@
 // One work-group holds 256 centroid rows (256/C query blocks of one head) and
 // streams that head's key means twice, 32 blocks per tile, through LDS (the
 // means arrive in their scoring form, written by the key-means kernel):
-//   pass 1: per-centroid running max and sum of exp2 (the softmax normaliser);
+//   pass 1: per-centroid sum of exp2 (the softmax normaliser), taken against a
+//           reference that trails the running max: the reference moves to
+//           the max only on the rare tiles where a term would pass 2^60, so
+//           most tiles take no max at all (fp32 sums have the range for it);
 //   pass 2: p = exp2(logit + log2 w_c - lse_c), summed over the C centroids of
 //           each query block and written to S.
 // Two precisions of the dot products, both accumulated in fp32:
@@ -248,16 +251,31 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
     auto epi1 = [&](const f32x16& x, int, int stage) {
       // logit = fac * x, fac a positive power of two (1 for split operands)
       const float fac = kF16 ? tsc[stage] * fac_mu : 1.f;
-      float tmax = -INFINITY;
+      auto tile_sum = [&]() {
+        float ps = 0.f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, x[v]);
-      const f32x2 tp = pair_x32(tmax);
-      tmax = fmaxf(tp[0], tp[1]) * fac;  // finite: every tile has a valid key
-      const float m_new = fmaxf(m_run, tmax);
-      s_run *= __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+        for (int v = 0; v < 16; ++v) ps += __builtin_amdgcn_exp2f(fmaf(x[v], fac, -m_run));
+        return ps;
+      };
+      float ps = tile_sum();
+      // the tile's sum above 2^60 on any lane (or inf / NaN while the reference
+      // is still -inf): move the reference to the running max, rescale the sum,
+      // and sum the tile again.  The empty asm on a copy of the logits keeps the
+      // max on this rare path (the compiler would otherwise hoist it)
+      if (__builtin_expect(__any(__float_as_uint(ps) > 0x5d800000u), 0)) {
+        f32x16 xs = x;
+        asm volatile("" : "+v"(xs));
+        float tmax = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s_run += __builtin_amdgcn_exp2f(fmaf(x[v], fac, -m_run));
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, xs[v]);
+        const f32x2 tp = pair_x32(tmax);
+        tmax = fmaxf(tp[0], tp[1]) * fac;  // finite: every tile has a valid key
+        const float m_new = fmaxf(m_run, tmax);
+        s_run *= __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        ps = tile_sum();
+      }
+      s_run += ps;
     };
     run_pass(hbase, lbase, mma1, fix1, epi1);
   }
