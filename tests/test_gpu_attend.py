@@ -95,9 +95,13 @@ def test_empty_rows_invalid_ids_and_overflowed_plan(dtype, v16):
     op = oracle_problem(wl)
     prob = lib_problem(wl)
     R, nkb = op.R, op.n_kb
-    # row 0: empty; row 1: blocks incl. out-of-range ids (skipped); row 2..: a few blocks
-    rows = [[], [0, 5, nkb + 3, -1, 17], [1, 2, 3]] + [[4 * r, 4 * r + 1] for r in range(3, R)]
-    lws = [[], [0.0, 1.0, 9.0, 9.0, 0.5], [0.0, 0.0, 2.0]] + [[0.3, 0.0] for _ in range(3, R)]
+    # row 0: empty; row 1: blocks incl. out-of-range ids (skipped); row 2: a whole first
+    # chunk of out-of-range ids (8 groups) and two more before three valid blocks; row 3..:
+    # a few blocks
+    bad = [-1, nkb, nkb + 7, -5] * 2 + [-1, nkb]
+    rows = [[], [0, 5, nkb + 3, -1, 17], bad + [1, 2, 3]] + [[4 * r, 4 * r + 1] for r in range(3, R)]
+    lws = [[], [0.0, 1.0, 9.0, 9.0, 0.5], [9.0] * len(bad) + [0.0, 0.0, 2.0]] + \
+        [[0.3, 0.0] for _ in range(3, R)]
     rp = np.cumsum([0] + [len(x) for x in rows])
     ci = np.array(sum(rows, []), np.int32)
     lw = np.array(sum(lws, []), np.float32)
@@ -114,6 +118,9 @@ def test_empty_rows_invalid_ids_and_overflowed_plan(dtype, v16):
     ref, rl = oracle.attend_row(q, k, v, op, 1, np.array([c for c, _ in valid], np.int32),
                                 np.array([w for _, w in valid], np.float32))
     check_output(torch.from_numpy(o[0, 0, 128:256]), ref, dtype, "row with invalid ids")
+    ref2, _ = oracle.attend_row(q, k, v, op, 2, np.array([1, 2, 3], np.int32),
+                                np.array([0.0, 0.0, 2.0], np.float32))
+    check_output(torch.from_numpy(o[0, 0, 256:384]), ref2, dtype, "row led by a chunk of invalid ids")
     # a plan whose status says it overflowed: every row empty
     gp.status = torch.ones(1, dtype=torch.int32, device="cuda")
     o2, lse2 = ab.attend(dq, dk, dv, gp, problem=prob, return_lse=True)
