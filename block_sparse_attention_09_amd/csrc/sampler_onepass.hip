@@ -7,7 +7,9 @@
 // One pass over the rows (k_sip_plan): a work-group solves pi for its row,
 // draws, keeps the row's kept-block bitmask in LDS, takes its offset in the
 // plan from the counts of the rows before it (decoupled look-back over
-// per-row records, rows handed out in ticket order), and writes row_ptr and
+// per-row records, the single-pass scan of Merrill and Garland, "Single-pass
+// Parallel Prefix Scan with Decoupled Look-back", 2016; rows handed out in
+// ticket order), and writes row_ptr and
 // the ascending block ids with logw = -ln(pi) (float64 log, rounded to fp32;
 // 0 where pi = 1) while its scores are still in LDS, so the score matrix is
 // read once and no scan or fill launch follows.  Forced (text) blocks follow
