@@ -4,7 +4,10 @@ The plan is built by the caller (random kept blocks, ascending per row) and
 given to both sides, so these tests isolate the attention kernels:
   * sharp logits (q and k scaled so that scale * q.k has a spread of tens of
     nats): the running max moves often and the accumulators are rescaled;
-  * a row max that rises chunk after chunk (every chunk forces a rescale);
+  * a row max that rises chunk after chunk (the softmax reference trails it and
+    is moved, with a rescale of the accumulators, many times along the row);
+  * the same two on the dense path (ragged N: a partial last key chunk and a
+    partial last query block), with the fp16-V form bit-identical to it;
   * large log-weight shifts (pi down to ~1e-13, logw up to 30);
   * large values (|v| ~ 1e3): the bar scales with the values, max-abs
     1e-2 * 1e3 (outputs are averages of values that partly cancel, while the
@@ -65,6 +68,23 @@ def _run(name, q, k, v, dtype, frac=0.3, logw_hi=3.0, seed=0, v_scale=1.0):
     assert np.abs(lh - L).max() <= LSE_TOL[dtype] * max(1.0, np.abs(L).max() / 8)
 
 
+def _run_dense(name, q, k, v, dtype):
+    B, H, N, D = q.shape
+    op = oracle.Problem(B=B, H=H, N=N, D=D)
+    O, L = oracle.dense(q, k, v, op)
+    prob = ab.Problem(B, H, N, D, dtype=dtype)
+    dq, dk, dv = (to_dev(x, dtype) for x in (q, k, v))
+    o, lse = ab.dense(dq, dk, dv, problem=prob, return_lse=True)
+    if dtype == "bf16":
+        o16, lse16 = ab.dense(dq, dk, ab.v_to_f16(dv, prob), problem=prob, return_lse=True)
+    torch.cuda.synchronize()
+    say(f"{name} dense {dtype}: |logit| spread up to {np.abs(L).max():.1f}")
+    check_output(o, O, dtype, f"{name} dense {dtype}")
+    assert np.abs(lse.cpu().numpy() - L).max() <= LSE_TOL[dtype] * max(1.0, np.abs(L).max() / 8)
+    if dtype == "bf16":
+        assert torch.equal(o16, o) and torch.equal(lse16, lse)
+
+
 def _qkv(seed, N, D, dtype, qk_scale=1.0, v_scale=1.0):
     rng = np.random.default_rng(seed)
     q = (qk_scale * rng.standard_normal((1, 2, N, D))).astype(np.float32)
@@ -91,6 +111,28 @@ def test_rising_max_rescales_every_chunk(dtype, D):
     q = round_like(q + 2.0 * d, dtype)
     k = round_like(k + ramp * d * np.sqrt(D) / 2.0, dtype)
     _run("rising max", q, k, v, dtype, frac=0.5)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_dense_sharp_logits(dtype, D):
+    q, k, v = _qkv(4, 2044, D, dtype, qk_scale=5.0)
+    _run_dense("sharp", q, k, v, dtype)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_dense_rising_max(dtype, D):
+    # logits rise along the keys: by 120 nats on the bf16 path, whose reference then
+    # moves every few chunks; by 40 on the fp32 path, whose fp32 logits at the
+    # steeper ramp (|logit| ~ 300) carry rounding that alone nears the 1e-4 bar
+    N = 2044
+    q, k, v = _qkv(5, N, D, dtype)
+    top = 120.0 if dtype == "bf16" else 40.0
+    ramp = np.linspace(0.0, top, N, dtype=np.float32)[None, None, :, None]
+    d = np.zeros((1, 1, 1, D), dtype=np.float32)
+    d[..., 0] = 1.0
+    q = round_like(q + 2.0 * d, dtype)
+    k = round_like(k + ramp * d * np.sqrt(D) / 2.0, dtype)
+    _run_dense("rising max", q, k, v, dtype)
 
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
