@@ -216,9 +216,11 @@ __global__ __launch_bounds__(kSampT) void k_sip_plan(
   }
 }
 
-// scores staged in LDS up to 150 KB (38400 blocks); with the mask words and
-// their 16-bit prefixes that is 157.2 KB of the 160 KB
-constexpr size_t kOnePassLdsMax = 150 * 1024;
+// scores staged in LDS up to 74 KB (18 944 blocks): with the mask words and
+// their 16-bit prefixes two work-groups still fit on a CU (158.3 KB at
+// 18 900 blocks); longer rows are read from L2 (as in the count kernel of
+// the three-kernel sampler)
+constexpr size_t kOnePassLdsMax = 74 * 1024;
 
 template <bool kLds>
 static hipError_t launch_onepass_t(const Shape& s, const float* S, double budget, uint64_t seed,

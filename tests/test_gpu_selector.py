@@ -132,8 +132,12 @@ SAMPLER = [
     (dict(B=1, H=1, N=4096, D=128), 1.0, 2.0, None),
     (dict(B=1, H=1, N=4096 + 256, D=128, n_forced_tail=256), 0.1, 3.0, None),
     (dict(B=2, H=3, N=2048, D=128), 0.25, 6.0, None),
-    # n_kbs = 40000 > what fits in LDS: the global-memory variant
+    # n_kbs = 40000: rows read from memory (too long to stage in LDS)
     (dict(B=1, H=1, N=160000, D=128), 0.05, 3.0, [0, 1, 7, 500, 1249]),
+    # n_kbs = 20480: the longest rows staged in LDS (80 KB, two work-groups per CU)
+    (dict(B=1, H=1, N=81920, D=64), 0.1, 3.0, [0, 1, 319, 639]),
+    # n_kbs = 20484: the shortest rows read from memory
+    (dict(B=1, H=1, N=81936, D=64), 0.1, 3.0, [0, 5, 640]),
 ]
 
 
@@ -185,7 +189,7 @@ PLAN_PATHS = {
     "bf16_mid_all": (SEL["bf16_mid"], 1.0),
     "tiny_f32": (SEL["tiny_f32"], 0.3),
     "bf16_d64_b2": (SEL["bf16_d64_b2"], 0.05),
-    # 38 000 key blocks: a row of 152 000 bytes, near the LDS limit of the count kernel
+    # 38 000 key blocks: a row of 152 000 bytes, read from memory by the count kernel
     "bf16_long_row": (Workload("L", B=1, H=1, D=64, grid=(19, 40, 200)), 0.1),
 }
 
