@@ -187,11 +187,12 @@ __global__ __launch_bounds__(kSampT) void k_sip_fill(const float* __restrict__ S
   }
 }
 
-// A row is staged in LDS only while two work-groups still fit on a CU; a
-// longer row is read again from L2 by the draws.  (Measured at 29 700 blocks,
-// 118.8 KB: staged, one work-group per CU, 1.66 ms; read from L2, 1.16 ms.
-// At 18 900 blocks staging wins, 0.785 against 0.825 ms.)
-constexpr size_t kSampLdsMax = 80 * 1024;
+// A row is staged in LDS only while two work-groups still fit on a CU (79 KB
+// of scores each, with room for the static LDS and the allocation granule);
+// a longer row is read again from L2 by the draws.  (Measured at 29 700
+// blocks, 118.8 KB: staged, one work-group per CU, 1.66 ms; read from L2,
+// 1.16 ms.  At 18 900 blocks staging wins, 0.785 against 0.825 ms.)
+constexpr size_t kSampLdsMax = 79 * 1024;
 
 template <bool kLds>
 static hipError_t launch_sampler_t(const Shape& s, const float* S, double budget, uint64_t seed,

@@ -134,10 +134,10 @@ SAMPLER = [
     (dict(B=2, H=3, N=2048, D=128), 0.25, 6.0, None),
     # n_kbs = 40000: rows read from memory (too long to stage in LDS)
     (dict(B=1, H=1, N=160000, D=128), 0.05, 3.0, [0, 1, 7, 500, 1249]),
-    # n_kbs = 20480: the longest rows staged in LDS (80 KB, two work-groups per CU)
-    (dict(B=1, H=1, N=81920, D=64), 0.1, 3.0, [0, 1, 319, 639]),
-    # n_kbs = 20484: the shortest rows read from memory
-    (dict(B=1, H=1, N=81936, D=64), 0.1, 3.0, [0, 5, 640]),
+    # n_kbs = 20224: the longest rows staged in LDS (79 KB, two work-groups per CU)
+    (dict(B=1, H=1, N=80896, D=64), 0.1, 3.0, [0, 1, 315, 631]),
+    # n_kbs = 20228: the shortest rows read from memory
+    (dict(B=1, H=1, N=80912, D=64), 0.1, 3.0, [0, 5, 632]),
 ]
 
 
