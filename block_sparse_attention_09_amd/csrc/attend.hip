@@ -43,7 +43,8 @@
 //     max passes it by more than 8, log2 units), rescale the accumulators
 //     and form them again.  Most chunks take no max at all;
 //   * work-groups run in plan-row order, so all XCDs share one head at a time
-//     and its K/V stays resident in the Infinity Cache.
+//     and its K/V stays resident in the Infinity Cache; a layer whose whole
+//     K/V fits that cache gives each XCD a contiguous range of rows instead.
 // fp32 kernel: plain fp32 arithmetic (one thread per query), used for fp32
 // problems.
 #include "common.h"
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(256, 3) void k_attend_bf16(
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const float* __restrict__ logw, int64_t capacity,
     const int32_t* __restrict__ status, uint16_t* __restrict__ O, float* __restrict__ lse, int N,
-    int n_qb, int n_kb, int R, float scale_log2, int lkb) {
+    int n_qb, int n_kb, int R, float scale_log2, int lkb, int xcd_contig) {
   constexpr int KS = D / 16;          // QK^T k-steps
   constexpr int DT = D / 32;          // PV output tiles
   constexpr int CPR = D / 8;          // 16-byte chunks per row
@@ -140,12 +141,15 @@ __global__ __launch_bounds__(256, 3) void k_attend_bf16(
   __shared__ __align__(16) uint16_t Vs[2][CK * D];
   __shared__ float lwb[2][NG];
 
-  // Plan rows in launch order: the dispatcher deals consecutive work-groups to
-  // the 8 XCDs in turn, so all XCDs work on the same head at once and that
-  // head's K/V (38.7 MB at 75600 tokens) stays in the 256 MB Infinity Cache.
-  // (Giving each XCD its own contiguous rows raised the L2 hit rate but
-  // spread the XCDs over 8 heads, and measured slower.)
-  const int r = blockIdx.x;
+  // Row order.  The dispatcher deals consecutive work-groups to the 8 XCDs in
+  // turn.  Large layers take rows in plan order, so all XCDs work on the same
+  // head at once and that head's K/V (38.7 MB at 75600 tokens) stays in the
+  // 256 MB Infinity Cache (giving each XCD its own contiguous rows there
+  // spreads the XCDs over 8 heads and measured 4% slower).  When the layer's
+  // whole K/V fits the Infinity Cache (xcd_contig), each XCD takes a
+  // contiguous range of rows instead, so its L2 serves fewer heads at a time
+  // (2% faster at 12 heads of 32760 tokens).
+  const int r = xcd_contig ? xcd_remap(blockIdx.x, R) : (int)blockIdx.x;
   const int qb = r % n_qb;
   const int64_t bh = r / n_qb;
   const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hh = lane >> 5;
@@ -635,9 +639,12 @@ static void launch_attend_t(const Shape& s, const void* Q, const void* K, const 
   if (kGather)
     while ((1 << lkb) < s.kv_block) ++lkb;
   if (s.bf16) {
+    // K and V (2 bytes an element each) of the whole layer within 224 MB: the
+    // rows of each XCD are taken as one contiguous range
+    const int xcd_contig = (size_t)s.B * s.H * s.N * s.D * 4 <= ((size_t)224 << 20) ? 1 : 0;
     k_attend_bf16<D, kGather, kV16><<<s.R, 256, 0, st>>>(
         (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, row_ptr, col_idx, logw,
-        capacity, status, (uint16_t*)O, lse, s.N, s.n_qb, s.n_kb, s.R, sl2, lkb);
+        capacity, status, (uint16_t*)O, lse, s.N, s.n_qb, s.n_kb, s.R, sl2, lkb, xcd_contig);
   } else {
     k_attend_f32<D, kGather><<<s.R, 128, 0, st>>>(
         (const float*)Q, (const float*)K, (const float*)V, row_ptr, col_idx, logw, capacity,
