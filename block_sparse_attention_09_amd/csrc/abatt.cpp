@@ -80,7 +80,7 @@ abatt_status make_dense_shape(const abatt_problem_t* p, Shape* s) {
 }
 
 struct PlanWs {
-  size_t kmean, mu, w, S, sampler, total;
+  size_t kmean, mu, w, S, partial, sampler, total;
 };
 
 // the sampler's scratch, for either sampler
@@ -100,6 +100,8 @@ PlanWs plan_ws_layout(const Shape& s) {
   off = align_up(off + (size_t)s.R * s.n_clusters * sizeof(float));
   l.S = off;
   off = align_up(off + (size_t)s.R * s.n_kbs * sizeof(float));
+  l.partial = off;
+  off = align_up(off + abatt::scores_partial_bytes(s));
   l.sampler = off;
   off = align_up(off + sampler_region(s));
   l.total = off;
@@ -126,7 +128,7 @@ hipError_t run_scores(const Shape& s, const PlanWs& l, char* ws, const void* Q, 
     e = abatt::launch_key_means_split(s, K, kplanes, stream);
   }
   if (e == hipSuccess) e = abatt::launch_kmeans(s, Q, mu, w, stream);
-  if (e == hipSuccess) e = abatt::launch_scores(s, mu, w, kplanes, tscale, S, stream);
+  if (e == hipSuccess) e = abatt::launch_scores(s, mu, w, kplanes, tscale, S, ws + l.partial, stream);
   return e;
 }
 

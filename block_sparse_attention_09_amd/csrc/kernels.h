@@ -32,9 +32,13 @@ hipError_t launch_key_means_f16(const Shape& s, const void* K, uint16_t* kh, flo
 hipError_t launch_kmeans(const Shape& s, const void* Q, float* mu, float* w, hipStream_t st);
 
 // score.hip: S [R, n_kbs] fp32 from centroids, weights and the key means in
-// their scoring form (split planes, tscale null; or the scaled fp16 plane)
+// their scoring form (split planes, tscale null; or the scaled fp16 plane).
+// Layers with few work-groups split each group's key tiles over two
+// launches; `partial` (scores_partial_bytes, 0 when unsplit) holds the
+// splits' partial normalisers between them.
+size_t scores_partial_bytes(const Shape& s);
 hipError_t launch_scores(const Shape& s, const float* mu, const float* w, const uint16_t* kplanes,
-                         const float* tscale, float* S, hipStream_t st);
+                         const float* tscale, float* S, void* partial, hipStream_t st);
 
 // sampler.hip: counts -> row_ptr -> col_idx/logw.  The sampler's scratch
 // (row counts, kept-block bitmasks, per-row solves) lives in `ws`.

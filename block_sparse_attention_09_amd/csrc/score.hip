@@ -43,14 +43,20 @@ constexpr int kScoreWaves = 8;                 // 256 centroid rows per work-gro
 constexpr int kScoreT = 64 * kScoreWaves;
 constexpr int kScoreStages = 3;                // LDS ring of key-mean tiles
 
-template <int D, int C, bool kF16>
+// kMode 0: both passes over every tile.  Layers with too few work-groups to
+// fill the chip split each group's tiles into nsplit ranges over two
+// launches: kMode 1 runs pass 1 over its range and writes each centroid's
+// partial (reference, sum) to `partial`; kMode 2 merges the partials of the
+// group into the normaliser and runs pass 2 over its range.
+template <int D, int C, bool kF16, int kMode>
 __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__ mu,
                                                        const float* __restrict__ w,
                                                        const uint16_t* __restrict__ kplanes,
                                                        const float* __restrict__ tscale,
                                                        float* __restrict__ S, int n_qb, int n_kbs,
                                                        int groups_per_head, int n_groups,
-                                                       int64_t plane_elems, float scale_log2) {
+                                                       int64_t plane_elems, float scale_log2,
+                                                       int nsplit, f32x2* __restrict__ partial) {
   constexpr int ROWS = 32 * kScoreWaves;  // centroid rows per work-group
   constexpr int G = ROWS / C;             // query blocks per work-group
   constexpr int KS = D / 16;              // MFMA k-steps
@@ -64,7 +70,10 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
   __shared__ float red[kScoreWaves];
   __shared__ float a_lds[ROWS];
 
-  const int gid = xcd_remap(blockIdx.x, n_groups);
+  // work-group -> (group, split): consecutive work-groups (one XCD) take
+  // consecutive groups of the same split, which share its key-mean tiles
+  const int gsp = xcd_remap(blockIdx.x, n_groups * nsplit);
+  const int gid = gsp % n_groups, spl = gsp / n_groups;
   const int bh = gid / groups_per_head;
   const int qb0 = (gid % groups_per_head) * G;
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63, l32 = lane & 31, hh = lane >> 5;
@@ -90,7 +99,10 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
   const uint16_t* hbase = kplanes + (int64_t)bh * n_kbs * D;
   const uint16_t* lbase = hbase + plane_elems;
   const int n_tiles = (n_kbs + 31) / 32;
-  const int tlast = n_tiles - 1;
+  // this work-group's tiles [t_begin, t_end)
+  const int t_begin = (int)((int64_t)n_tiles * spl / nsplit);
+  const int t_end = (int)((int64_t)n_tiles * (spl + 1) / nsplit);
+  const int tlast = t_end - 1;
   const float* tsbase = kF16 ? tscale + (int64_t)bh * n_tiles : nullptr;
 
   auto kop = [&](const uint16_t* base, int s) -> u32x4 {
@@ -140,19 +152,19 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
       if constexpr (kF16)
         if (t == 0) tsc[stage] = r.sc;
     };
-    load_tile(ra, 0);
+    load_tile(ra, t_begin);
     store_tile(ra, 0);
-    load_tile(rb, min(1, tlast));
+    load_tile(rb, min(t_begin + 1, tlast));
     store_tile(rb, 1);
-    load_tile(ra, min(2, tlast));
-    load_tile(rb, min(3, tlast));
+    load_tile(ra, min(t_begin + 2, tlast));
+    load_tile(rb, min(t_begin + 3, tlast));
     __syncthreads();
     f32x16 xa = mma(0), xb;
     int st = 0;  // stage of `tile`
     auto nxt = [](int s) { return s == kScoreStages - 1 ? 0 : s + 1; };
     // Each half-iteration's MFMAs and exp2 work form one branch-free block;
     // the MFMAs past the last tile read a stale stage and are discarded.
-    for (int tile = 0; tile < n_tiles; tile += 2) {
+    for (int tile = t_begin; tile < t_end; tile += 2) {
       const int s1 = nxt(st), s2 = nxt(s1);
       store_tile(ra, s2);
       load_tile(ra, min(tile + 4, tlast));
@@ -160,7 +172,7 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
       xb = mma(s1);
       epi(xa, tile, st);
       __syncthreads();
-      if (tile + 1 < n_tiles) {
+      if (tile + 1 < t_end) {
         store_tile(rb, st);  // stage of tile + 3
         load_tile(rb, min(tile + 5, tlast));
         fix(xb, tile + 1);
@@ -217,7 +229,7 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
 
   // ---------------- pass 1: softmax normaliser of every centroid ----------------
   float m_run = -INFINITY, s_run = 0.f;
-  {
+  if constexpr (kMode != 2) {
     auto mma1 = [&](int stage) {
       f32x16 x = {};
       if constexpr (kF16) {
@@ -278,10 +290,28 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
       s_run += ps;
     };
     run_pass(hbase, lbase, mma1, fix1, epi1);
-  }
-  {
     const f32x2 sp = pair_x32(s_run);
     s_run = sp[0] + sp[1];
+  }
+  if constexpr (kMode == 1) {
+    // this split's partial normaliser of every centroid row: the sum of
+    // exp2(logit - m_run) over the split's tiles, with its reference
+    if (hh == 0) partial[((int64_t)gid * nsplit + spl) * ROWS + crow] = f32x2{m_run, s_run};
+    return;
+  }
+  if constexpr (kMode == 2) {
+    // merge the group's partials: the largest reference M and the sum of
+    // every split's sum scaled by 2^(m_i - M)
+    const f32x2* pr = partial + (int64_t)gid * nsplit * ROWS + crow;
+    float M = -INFINITY;
+    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, pr[(int64_t)i * ROWS][0]);
+    float sum = 0.f;
+    for (int i = 0; i < nsplit; ++i) {
+      const f32x2 q = pr[(int64_t)i * ROWS];
+      sum += q[1] * __builtin_amdgcn_exp2f(q[0] - M);
+    }
+    m_run = M;
+    s_run = sum;
   }
   // log2 of (w_c / normaliser); -inf for an empty cluster
   const float a_c = log2f(wc) - (m_run + log2f(s_run));
@@ -360,31 +390,70 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
   run_pass(hbase, lbase, mma2, fix2, epi2);
 }
 
-template <int D, int C>
-static hipError_t launch_scores_t(const Shape& s, const float* mu, const float* w,
+// Splits of each group's tiles: enough work-groups for one round of two per
+// CU (512), with at least four tiles in a split.  The 14B and HunyuanVideo
+// layers have 720-760 groups and run unsplit.
+static int score_splits(const Shape& s, int n_groups) {
+  const int n_tiles = (s.n_kbs + 31) / 32;
+  int n = (512 + n_groups - 1) / n_groups;
+  const int cap = n_tiles / 4 > 1 ? n_tiles / 4 : 1;
+  return n < cap ? n : cap;
+}
+
+static int score_groups(const Shape& s) {
+  const int G = 32 * kScoreWaves / s.n_clusters;
+  return s.B * s.H * ((s.n_qb + G - 1) / G);
+}
+
+size_t scores_partial_bytes(const Shape& s) {
+  const int n_groups = score_groups(s);
+  const int ns = score_splits(s, n_groups);
+  return ns > 1 ? (size_t)n_groups * ns * (32 * kScoreWaves) * sizeof(f32x2) : 0;
+}
+
+template <int D, int C, bool kF16>
+static hipError_t launch_scores_m(const Shape& s, const float* mu, const float* w,
                                   const uint16_t* kplanes, const float* tscale, float* S,
-                                  hipStream_t st) {
+                                  void* partial, hipStream_t st) {
   constexpr int G = 32 * kScoreWaves / C;
   const int gph = (s.n_qb + G - 1) / G;
   const int n_groups = s.B * s.H * gph;
   const int64_t plane = (int64_t)s.B * s.H * s.n_kbs * s.D;
-  if (s.bf16)
-    k_scores<D, C, true><<<n_groups, kScoreT, 0, st>>>(mu, w, kplanes, tscale, S, s.n_qb, s.n_kbs,
-                                                       gph, n_groups, plane, s.scale * kLog2e);
-  else
-    k_scores<D, C, false><<<n_groups, kScoreT, 0, st>>>(mu, w, kplanes, nullptr, S, s.n_qb,
-                                                        s.n_kbs, gph, n_groups, plane,
-                                                        s.scale * kLog2e);
+  const int ns = score_splits(s, n_groups);
+  const float sl2 = s.scale * kLog2e;
+  f32x2* pr = static_cast<f32x2*>(partial);
+  if (ns == 1) {
+    k_scores<D, C, kF16, 0><<<n_groups, kScoreT, 0, st>>>(mu, w, kplanes, tscale, S, s.n_qb,
+                                                          s.n_kbs, gph, n_groups, plane, sl2,
+                                                          1, nullptr);
+    return hipGetLastError();
+  }
+  k_scores<D, C, kF16, 1><<<n_groups * ns, kScoreT, 0, st>>>(mu, w, kplanes, tscale, S, s.n_qb,
+                                                             s.n_kbs, gph, n_groups, plane, sl2,
+                                                             ns, pr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_scores<D, C, kF16, 2><<<n_groups * ns, kScoreT, 0, st>>>(mu, w, kplanes, tscale, S, s.n_qb,
+                                                             s.n_kbs, gph, n_groups, plane, sl2,
+                                                             ns, pr);
   return hipGetLastError();
 }
 
+template <int D, int C>
+static hipError_t launch_scores_t(const Shape& s, const float* mu, const float* w,
+                                  const uint16_t* kplanes, const float* tscale, float* S,
+                                  void* partial, hipStream_t st) {
+  if (s.bf16) return launch_scores_m<D, C, true>(s, mu, w, kplanes, tscale, S, partial, st);
+  return launch_scores_m<D, C, false>(s, mu, w, kplanes, nullptr, S, partial, st);
+}
+
 hipError_t launch_scores(const Shape& s, const float* mu, const float* w, const uint16_t* kplanes,
-                         const float* tscale, float* S, hipStream_t st) {
+                         const float* tscale, float* S, void* partial, hipStream_t st) {
   if (s.D == 128)
-    return s.n_clusters == 8 ? launch_scores_t<128, 8>(s, mu, w, kplanes, tscale, S, st)
-                             : launch_scores_t<128, 16>(s, mu, w, kplanes, tscale, S, st);
-  return s.n_clusters == 8 ? launch_scores_t<64, 8>(s, mu, w, kplanes, tscale, S, st)
-                           : launch_scores_t<64, 16>(s, mu, w, kplanes, tscale, S, st);
+    return s.n_clusters == 8 ? launch_scores_t<128, 8>(s, mu, w, kplanes, tscale, S, partial, st)
+                             : launch_scores_t<128, 16>(s, mu, w, kplanes, tscale, S, partial, st);
+  return s.n_clusters == 8 ? launch_scores_t<64, 8>(s, mu, w, kplanes, tscale, S, partial, st)
+                           : launch_scores_t<64, 16>(s, mu, w, kplanes, tscale, S, partial, st);
 }
 
 }  // namespace abatt

@@ -46,10 +46,13 @@ def test_sizes(lib):
     assert 16 * 25.6 < b <= ab.max_nnz(p)
     assert ab.nnz_bound(p, 1.0) == ab.max_nnz(p)
     ws = ab.plan_workspace_bytes(p)
-    # means + centroids + weights + scores + sampler scratch (row counts,
-    # kept-block bitmasks of 256/32 words per row, 16-byte row solves)
+    # means + centroids + weights + scores + the scorer's partial normalisers
+    # (2 groups of 256 centroid rows, each group's 8 key tiles in 2 splits, 8
+    # bytes per row and split) + sampler scratch (row counts, kept-block
+    # bitmasks of 256/32 words per row, 16-byte row solves)
     sampler = 16 * 4 + 16 * 8 * 4 + 16 * 16
-    need = 2 * 256 * 128 * 4 + 16 * 8 * 128 * 4 + 16 * 8 * 4 + 16 * 256 * 4 + sampler
+    partial = 2 * 2 * 256 * 8
+    need = 2 * 256 * 128 * 4 + 16 * 8 * 128 * 4 + 16 * 8 * 4 + 16 * 256 * 4 + partial + sampler
     assert need <= ws <= need + 8 * 256
     assert sampler <= ab.sampler_workspace_bytes(p) <= sampler + 4 * 256
     pf = prob(N=1024 + 256, n_forced_tail=256)
