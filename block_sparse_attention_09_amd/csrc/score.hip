@@ -390,14 +390,20 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
   run_pass(hbase, lbase, mma2, fix2, epi2);
 }
 
-// Splits of each group's tiles: enough work-groups for one round of two per
-// CU (512), with at least four tiles in a split.  The 14B and HunyuanVideo
-// layers have 720-760 groups and run unsplit.
+// Splits of each group's tiles: the fewest that fill the rounds of work-
+// groups (512 slots, two per CU) to 90%, with at least four tiles in a split.
+// 760 groups (14B) or 720 (HunyuanVideo) alone leave the second round half
+// empty: two splits each; 1480 (16 clusters) fill three rounds unsplit; 96
+// (1.3B) take five.
 static int score_splits(const Shape& s, int n_groups) {
   const int n_tiles = (s.n_kbs + 31) / 32;
-  int n = (512 + n_groups - 1) / n_groups;
   const int cap = n_tiles / 4 > 1 ? n_tiles / 4 : 1;
-  return n < cap ? n : cap;
+  for (int n = 1; n <= cap; ++n) {
+    const int64_t wgs = (int64_t)n_groups * n;
+    const int64_t rounds = (wgs + 511) / 512;
+    if (wgs * 10 >= rounds * 512 * 9) return n;
+  }
+  return cap;
 }
 
 static int score_groups(const Shape& s) {
