@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -112,22 +113,85 @@ size_t sampler_ws_bytes(const Shape& s) { return align_up(sampler_region(s)); }
 
 abatt_status hip_status(hipError_t e) { return e == hipSuccess ? ABATT_OK : ABATT_EHIP; }
 
+// A second stream per device, owned by the library (default priority), and
+// the two events that fork it from a caller's stream and join it back.
+struct Side {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+Side g_side[kMaxDevices];
+
+// The current device's side stream, created on first use; nullptr when there
+// is none to be had: creation failed, the device index is out of range, or
+// it does not exist yet and may not be created now (`may_create` false, or
+// `stream` under capture).  Called with g_side_mu held.
+Side* side_stream(hipStream_t stream, bool may_create) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  Side& sd = g_side[dev];
+  if (sd.s != nullptr) return &sd;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (!may_create || hipStreamIsCapturing(stream, &cs) != hipSuccess ||
+      cs != hipStreamCaptureStatusNone)
+    return nullptr;
+  Side n;
+  if (hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) == hipSuccess &&
+      hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) == hipSuccess &&
+      hipEventCreateWithFlags(&n.join, hipEventDisableTiming) == hipSuccess) {
+    sd = n;
+    return &sd;
+  }
+  if (n.join != nullptr) (void)hipEventDestroy(n.join);
+  if (n.fork != nullptr) (void)hipEventDestroy(n.fork);
+  if (n.s != nullptr) (void)hipStreamDestroy(n.s);
+  return nullptr;
+}
+
 // Key means in their scoring form, centroids and weights, scores.  The
 // key-mean region holds two bf16 planes (fp32 problems) or one fp16 plane
 // followed by the per-tile scales (bf16 problems), which fits in the same
 // space.
+//
+// The key means (K only, bound by HBM) and k-means (Q only, bound by the
+// latency of its Lloyd iterations) do not depend on each other, so they run
+// side by side: the key means on the side stream, forked from `stream` by an
+// event, k-means on `stream`, which waits for the side stream's join event
+// before the scorer.  The call thus stays ordered on `stream` and can be
+// captured into a graph.  Without a side stream both run on `stream`, one
+// after the other (the same results).
 hipError_t run_scores(const Shape& s, const PlanWs& l, char* ws, const void* Q, const void* K,
-                      float* mu, float* w, float* S, hipStream_t stream) {
+                      float* mu, float* w, float* S, hipStream_t stream, bool may_create = true) {
   uint16_t* kplanes = reinterpret_cast<uint16_t*>(ws + l.kmean);
-  float* tscale = nullptr;
+  float* tscale = s.bf16 ? reinterpret_cast<float*>(kplanes + (size_t)s.B * s.H * s.n_kbs * s.D)
+                         : nullptr;
+  auto key_means = [&](hipStream_t st) {
+    return s.bf16 ? abatt::launch_key_means_f16(s, K, kplanes, tscale, st)
+                  : abatt::launch_key_means_split(s, K, kplanes, st);
+  };
   hipError_t e;
-  if (s.bf16) {
-    tscale = reinterpret_cast<float*>(kplanes + (size_t)s.B * s.H * s.n_kbs * s.D);
-    e = abatt::launch_key_means_f16(s, K, kplanes, tscale, stream);
-  } else {
-    e = abatt::launch_key_means_split(s, K, kplanes, stream);
+  {
+    // one fork / join at a time: the events are shared by every call on the device
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    Side* sd = side_stream(stream, may_create);
+    if (sd == nullptr) {
+      e = key_means(stream);
+      if (e == hipSuccess) e = abatt::launch_kmeans(s, Q, mu, w, stream);
+    } else {
+      e = hipEventRecord(sd->fork, stream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(sd->s, sd->fork, 0);
+      if (e == hipSuccess) {
+        // joined whatever the launches return, so that the side stream never
+        // stays forked off a capture
+        const hipError_t ek = key_means(sd->s);
+        const hipError_t er = hipEventRecord(sd->join, sd->s);
+        const hipError_t em = abatt::launch_kmeans(s, Q, mu, w, stream);
+        const hipError_t ej = er == hipSuccess ? hipStreamWaitEvent(stream, sd->join, 0) : er;
+        e = ek != hipSuccess ? ek : (em != hipSuccess ? em : ej);
+      }
+    }
   }
-  if (e == hipSuccess) e = abatt::launch_kmeans(s, Q, mu, w, stream);
   if (e == hipSuccess) e = abatt::launch_scores(s, mu, w, kplanes, tscale, S, ws + l.partial, stream);
   return e;
 }
@@ -136,11 +200,11 @@ hipError_t run_scores(const Shape& s, const PlanWs& l, char* ws, const void* Q, 
 // onepass selects the one-pass sampler (the same plan).
 hipError_t run_plan(const Shape& s, const PlanWs& l, char* ws, const void* Q, const void* K,
                     double budget, uint64_t seed, const abatt_plan_t* plan, hipStream_t stream,
-                    bool onepass = false) {
+                    bool onepass = false, bool may_create = true) {
   float* mu = reinterpret_cast<float*>(ws + l.mu);
   float* w = reinterpret_cast<float*>(ws + l.w);
   float* S = reinterpret_cast<float*>(ws + l.S);
-  hipError_t e = run_scores(s, l, ws, Q, K, mu, w, S, stream);
+  hipError_t e = run_scores(s, l, ws, Q, K, mu, w, S, stream, may_create);
   if (e == hipSuccess)
     e = (onepass ? abatt::launch_sampler_onepass : abatt::launch_sampler)(
         s, S, budget, seed, ws + l.sampler, plan->row_ptr, plan->col_idx, plan->logw,
@@ -284,7 +348,9 @@ abatt_status abatt_plan_noalloc(const abatt_problem_t* p, const void* Q, const v
   void* ws = nullptr;
   hipError_t e = abatt::scratch_ptr(&ws);
   if (e != hipSuccess) return ABATT_EHIP;
-  return hip_status(run_plan(s, l, static_cast<char*>(ws), Q, K, budget, seed, plan, stream));
+  // creates no side stream (it uses one an earlier call made)
+  return hip_status(run_plan(s, l, static_cast<char*>(ws), Q, K, budget, seed, plan, stream,
+                             false, false));
 }
 
 abatt_status abatt_attend(const abatt_problem_t* p, const void* Q, const void* K, const void* V,

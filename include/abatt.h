@@ -31,12 +31,22 @@
  *     never allocates or frees device memory and never synchronises: each
  *     call checks its arguments on the host, enqueues kernels on `stream` and
  *     returns.  Scratch memory comes in through `workspace`.
+ *   - The plan calls (abatt_plan, abatt_plan_onepass, abatt_plan_noalloc,
+ *     abatt_scores) run their key-means kernel beside k-means on a second
+ *     stream that the library creates once per device (default priority,
+ *     kept until the process ends).  It is forked from `stream` by an event
+ *     and joined back by another before the scorer, so the call's work stays
+ *     ordered on `stream` and a graph captured from `stream` holds both
+ *     branches.  The side stream is never created while `stream` is under
+ *     capture, nor by abatt_plan_noalloc: without it both kernels run on
+ *     `stream`, with the same results.
  *   - Invalid arguments are reported synchronously, before any HIP call, as a
  *     negative abatt_status; nothing is enqueued then.  A failed launch gives
  *     ABATT_EHIP.  Device-side conditions (a plan that outgrew its capacity)
  *     are written to plan->status without a sync.  Faults inside kernels
  *     surface at the caller's next synchronisation.
- *   - The library holds no state between calls and is thread-safe.  Calls on
+ *   - Apart from those side streams the library holds no state between
+ *     calls, and it is thread-safe (a mutex orders the forks).  Calls on
  *     different streams need their own workspaces and plans.  The one
  *     exception is abatt_plan_noalloc, whose workspace is a static device
  *     array of the library shared by every call on a GPU (see there).
@@ -192,8 +202,9 @@ abatt_status abatt_plan_onepass(const abatt_problem_t *p, const void *Q, const v
  * abatt_plan, without the workspace: the plan workspace lives in a static
  * device array of ABATT_SCRATCH_BYTES inside the library, one per GPU,
  * held from the library's first use on that GPU until the process ends.
- * The call itself allocates and frees nothing; the caller still provides Q,
- * K and the plan buffers.
+ * The call itself allocates and frees nothing and creates no stream (it
+ * forks onto a side stream only when an earlier plan call on the GPU made
+ * one); the caller still provides Q, K and the plan buffers.
  *   - Returns ABATT_ESCRATCH, before any HIP call, when
  *     abatt_plan_workspace_bytes(p) > ABATT_SCRATCH_BYTES (call it per group
  *     of heads instead: the plan rows of a head depend on that head only).

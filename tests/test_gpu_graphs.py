@@ -1,10 +1,11 @@
 """The library under HIP graph capture and on concurrent streams.
 
 Every entry point only enqueues kernels on the caller's stream (no memsets,
-copies, allocations or synchronisations), so a plan + attend sequence (also
-with the V conversion of the fp16-V form) can be captured once and replayed,
-and calls on different streams with their own
-workspaces and plans do not interfere.  Checked bit for bit against eager
+copies, allocations or synchronisations; the plan's key means run on the
+library's side stream, forked from the caller's stream and joined back to
+it), so a plan + attend sequence (also with the V conversion of the fp16-V
+form) can be captured once and replayed, and calls on different streams with
+their own workspaces and plans do not interfere.  Checked bit for bit against eager
 calls: several replays with eager work and synchronisations between them, and
 two streams (default priority) working at once.
 """
@@ -115,3 +116,55 @@ def test_two_streams_at_once():
             assert torch.equal(pl.col_idx[:n], rpl.col_idx[:n])
             assert torch.equal(o, ro)
     say("two streams: identical to sequential calls")
+
+
+_FRESH = r"""
+import torch
+import block_sparse_attention_09_amd as ab
+from helpers import lib_problem, to_dev
+from workloads import Workload, make_qkv
+
+wl = Workload("g", B=1, H=2, D=128, grid=(3, 16, 32), dtype="bf16", seed=5, n_text=64)
+q, k, v = (to_dev(x, "bf16") for x in make_qkv(wl))
+prob = lib_problem(wl)
+budget, seed = 0.15, 3
+# load the plan's kernels without making the side stream (noalloc never does)
+ab.plan_noalloc(q, k, budget, seed=seed, problem=prob)
+torch.cuda.synchronize()
+ws = ab.workspace(prob, q.device)
+pl = ab.empty_plan(prob, ab.nnz_bound(prob, budget), q.device)
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):  # no side stream yet: the captured plan runs on one stream
+    ab.plan(q, k, budget, seed=seed, problem=prob, ws=ws, out=pl)
+g.replay()
+torch.cuda.synchronize()
+ref = ab.plan(q, k, budget, seed=seed, problem=prob)  # eager: makes the side stream
+torch.cuda.synchronize()
+n = ref.nnz()
+for rep in range(2):
+    assert torch.equal(pl.row_ptr, ref.row_ptr), rep
+    assert torch.equal(pl.col_idx[:n], ref.col_idx[:n]), rep
+    assert torch.equal(pl.logw[:n], ref.logw[:n]), rep
+    pl.col_idx.fill_(-1)
+    g.replay()
+    torch.cuda.synchronize()
+print("fresh-process capture ok", n)
+"""
+
+
+def test_plan_captured_before_side_stream():
+    """A plan captured before the library has its side stream (the first plan
+    call of a process, under capture) runs on the captured stream alone; its
+    replays equal eager plans made afterwards with the side stream."""
+    import os
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    env = dict(os.environ)
+    env["PYTHONPATH"] = os.pathsep.join([os.path.dirname(here), here, env.get("PYTHONPATH", "")])
+    say("fresh process: plan captured before the side stream exists")
+    r = subprocess.run([sys.executable, "-c", _FRESH], env=env, capture_output=True, text=True,
+                       timeout=110)
+    say(r.stdout.strip()[-300:])
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "fresh-process capture ok" in r.stdout
