@@ -223,25 +223,34 @@ __device__ __forceinline__ const float* stage_row(const float* g, int n, float* 
 
 // pi_j * 2^32, exactly: pi_of scaled by a power of two (c32 = c * 2^32, and
 // a power-of-two factor commutes with the product's rounding).
+// (Selects rather than branches on the per-block conditions; the mode is the
+// same for the whole row.)
 __device__ __forceinline__ double pi_x32(float s, const PiSolve& ps, double c32) {
-  if (ps.mode == 0) return kTwo32;
-  if (!(s > 0.f)) return 0.0;
-  if (ps.mode == 1 || s >= ps.theta) return kTwo32;
-  return c32 * (double)s;
+  const double p = (ps.mode == 1 || s >= ps.theta) ? kTwo32 : c32 * (double)s;
+  return ps.mode == 0 ? kTwo32 : (s > 0.f ? p : 0.0);
 }
 
 // Kept-bit mask (4 bits) of blocks 4g..4g+3: one Philox call (counter g),
-// word k for block 4g + k.
+// word k for block 4g + k.  The four scores are read (one 16-byte read when
+// the row is 16-byte aligned and the group lies inside it) before the Philox
+// rounds, which then cover the read's latency.
 __device__ __forceinline__ uint32_t draw_group(const float* s, int n, int g, int qb, int h, int b,
                                                uint64_t seed, const PiSolve& ps, double c32) {
+  float v[4];
+  if (4 * g + 3 < n && (reinterpret_cast<uintptr_t>(s) & 15) == 0) {
+    const f32x4 q = reinterpret_cast<const f32x4*>(s)[g];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = q[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = 4 * g + k < n ? s[4 * g + k] : 0.f;
+  }
   uint32_t c[4] = {(uint32_t)g, (uint32_t)qb, (uint32_t)h, (uint32_t)b};
   philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
   uint32_t mask = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int j = 4 * g + k;
-    if (j < n && sip_keep(c[k], pi_x32(s[j], ps, c32))) mask |= 1u << k;
-  }
+  for (int k = 0; k < 4; ++k)
+    mask |= (uint32_t)((4 * g + k < n) & sip_keep(c[k], pi_x32(v[k], ps, c32))) << k;
   return mask;
 }
 
