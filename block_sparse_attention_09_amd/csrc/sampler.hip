@@ -7,11 +7,12 @@
 // block carries the Horvitz-Thompson weight 1/pi, applied as the logit shift
 // log(1/pi).
 //
-// Per plan row (one work-group, the score row staged in LDS):
+// Per plan row (one work-group; the count kernel reads the score row in
+// place, the one-pass kernel stages it in LDS when it fits):
 //   * pi: m = budget * n expected blocks; repeat c = (m - #certain) /
 //     sum(uncertain positive scores) and make every uncertain block with
 //     c*s >= 1 certain, until none is added (the first round's count, sum
-//     and maximum are gathered while the row is staged).  The certain set
+//     and maximum are gathered in the row's first read).  The certain set
 //     is always a top set of the scores, so it is held as a threshold theta
 //     (certain iff s >= theta).  float64 throughout; sums are fixed-order
 //     tree reductions, so every run gives the same bits.
@@ -32,19 +33,19 @@
 
 namespace abatt {
 
-template <bool kLds>
+// The row is read in place: its first pass gathers the statistics, the
+// solve (when it iterates) and the draws read it again from L2.
 __global__ __launch_bounds__(kSampT) void k_sip_count(const float* __restrict__ S, int n,
                                                      int n_forced, int n_qb, int H,
                                                      double budget, uint64_t seed,
                                                      int32_t* __restrict__ counts,
                                                      uint32_t* __restrict__ masks,
                                                      PiSolve* __restrict__ solves) {
-  extern __shared__ __align__(16) float srow[];
   __shared__ Red red;
   const int r = blockIdx.x;
   const int qb = r % n_qb, bh = r / n_qb, h = bh % H, b = bh / H;
   RowStats st;
-  const float* s = stage_row<kLds>(S + (int64_t)r * n, n, srow, st);
+  const float* s = stage_row<false>(S + (int64_t)r * n, n, nullptr, st);
   const PiSolve ps = solve_pi(s, n, budget, st, red);
   const double c32 = ps.c * kTwo32;
   const int groups = (n + 3) / 4;
@@ -187,31 +188,22 @@ __global__ __launch_bounds__(kSampT) void k_sip_fill(const float* __restrict__ S
   }
 }
 
-// A row is staged in LDS only while two work-groups still fit on a CU (79 KB
-// of scores each, with room for the static LDS and the allocation granule);
-// a longer row is read again from L2 by the draws.  (Measured at 29 700
-// blocks, 118.8 KB: staged, one work-group per CU, 1.66 ms; read from L2,
-// 1.16 ms.  At 18 900 blocks staging wins, 0.785 against 0.825 ms.)
-constexpr size_t kSampLdsMax = 79 * 1024;
-
-template <bool kLds>
-static hipError_t launch_sampler_t(const Shape& s, const float* S, double budget, uint64_t seed,
-                                   void* ws, int32_t* row_ptr, int32_t* col_idx, float* logw,
-                                   int64_t capacity, int32_t* status, hipStream_t st) {
-  const size_t lds = kLds ? (size_t)s.n_kbs * sizeof(float) : 0;
+// The count kernel reads its row in place rather than staging it in LDS:
+// without the 75.6 KB of LDS per row, four work-groups share a CU instead of
+// two, and the draws read each group's four scores in one 16-byte load ahead
+// of the Philox rounds.  (At 18 900 blocks: 0.619 ms in place, 0.709 ms
+// staged.)
+hipError_t launch_sampler(const Shape& s, const float* S, double budget, uint64_t seed,
+                          void* ws, int32_t* row_ptr, int32_t* col_idx, float* logw,
+                          int64_t capacity, int32_t* status, hipStream_t st) {
   const int n_forced = s.n_kb - s.n_kbs;
   SamplerWs l = sampler_ws_layout(s);
   char* base = static_cast<char*>(ws);
   int32_t* counts = reinterpret_cast<int32_t*>(base + l.counts);
   uint32_t* masks = reinterpret_cast<uint32_t*>(base + l.masks);
   PiSolve* solves = reinterpret_cast<PiSolve*>(base + l.solves);
-  if (kLds) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_sip_count<kLds>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  k_sip_count<kLds><<<s.R, kSampT, lds, st>>>(S, s.n_kbs, n_forced, s.n_qb, s.H, budget, seed,
-                                              counts, masks, solves);
+  k_sip_count<<<s.R, kSampT, 0, st>>>(S, s.n_kbs, n_forced, s.n_qb, s.H, budget, seed, counts,
+                                      masks, solves);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   k_scan<<<1, 1024, 0, st>>>(counts, s.R, row_ptr, capacity, status);
@@ -232,14 +224,5 @@ SamplerWs sampler_ws_layout(const Shape& s) {
   return l;
 }
 
-hipError_t launch_sampler(const Shape& s, const float* S, double budget, uint64_t seed,
-                          void* ws, int32_t* row_ptr, int32_t* col_idx, float* logw,
-                          int64_t capacity, int32_t* status, hipStream_t st) {
-  if ((size_t)s.n_kbs * sizeof(float) <= kSampLdsMax)
-    return launch_sampler_t<true>(s, S, budget, seed, ws, row_ptr, col_idx, logw, capacity,
-                                  status, st);
-  return launch_sampler_t<false>(s, S, budget, seed, ws, row_ptr, col_idx, logw, capacity,
-                                 status, st);
-}
 
 }  // namespace abatt
