@@ -28,7 +28,7 @@ CASES = {
                                  kv_block=128), 0.5),
     "bf16_all": (Workload("m", B=1, H=2, D=128, grid=(6, 16, 24)), 1.0),
     # 18 944 key blocks: the longest rows whose scores the one-pass kernel stages in
-    # LDS (74 KB); the three-kernel count stages them too (up to 20 224)
+    # LDS (74 KB); the three-kernel count kernel reads every row in place
     "bf16_row_staged": (Workload("L", B=1, H=1, D=64, grid=(1, 4, 18944)), 0.1),
     # 18 948 key blocks: the one-pass kernel reads them from the workspace instead
     "bf16_row_past_stage": (Workload("P", B=1, H=1, D=64, grid=(1, 4, 18948)), 0.1),

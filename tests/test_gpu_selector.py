@@ -132,11 +132,13 @@ SAMPLER = [
     (dict(B=1, H=1, N=4096, D=128), 1.0, 2.0, None),
     (dict(B=1, H=1, N=4096 + 256, D=128, n_forced_tail=256), 0.1, 3.0, None),
     (dict(B=2, H=3, N=2048, D=128), 0.25, 6.0, None),
-    # n_kbs = 40000: rows read from memory (too long to stage in LDS)
+    # long rows (the count kernel reads every row in place; its first read
+    # issues at most 10 loads of 16 bytes per thread at a time, 20 480 blocks):
+    # n_kbs = 40000, two rounds of loads
     (dict(B=1, H=1, N=160000, D=128), 0.05, 3.0, [0, 1, 7, 500, 1249]),
-    # n_kbs = 20224: the longest rows staged in LDS (79 KB, two work-groups per CU)
+    # n_kbs = 20224 and 20228: rows just under 20 480 blocks, the longest that
+    # one round of loads covers
     (dict(B=1, H=1, N=80896, D=64), 0.1, 3.0, [0, 1, 315, 631]),
-    # n_kbs = 20228: the shortest rows read from memory
     (dict(B=1, H=1, N=80912, D=64), 0.1, 3.0, [0, 5, 632]),
 ]
 
