@@ -175,6 +175,7 @@ __global__ __launch_bounds__(256) void k_kmeans_mfma(const uint16_t* __restrict_
   __shared__ __align__(16) uint16_t lds[QB * XS];
   __shared__ __align__(16) uint16_t oh[16 * OS];  // onehot[c][p] of the last assignment
   __shared__ __align__(16) float npart[4][16];    // per-wave partial |mu_c|^2
+  __shared__ int wchg[2][4];                      // per-wave "assignment changed", by iteration parity
   uint16_t* xs = lds;
   uint16_t* planes = lds;  // [3][16][XS] after set-up
 
@@ -319,8 +320,17 @@ __global__ __launch_bounds__(256) void k_kmeans_mfma(const uint16_t* __restrict_
     }
     // an assignment equal to the previous one is a fixed point: the update
     // would reproduce the centroids and counts (and so would every later
-    // iteration), so the loop ends with the result it would reach at iters
-    if (!__syncthreads_or(changed)) break;
+    // iteration), so the loop ends with the result it would reach at iters.
+    // One vote per wave and one barrier (which also publishes the one-hot
+    // matrix); the two flag sets alternate, so a set is rewritten only after
+    // the barrier that ends the next iteration.
+    {
+      const bool wc = __any(changed);
+      if (l == 0) wchg[it & 1][w] = wc;
+      __syncthreads();
+      const int* f = wchg[it & 1];
+      if (!(f[0] | f[1] | f[2] | f[3])) break;
+    }
     // update: member sums on the matrix cores; counts from the one-hot bits
     f32x4 sum[UT];
 #pragma unroll
