@@ -100,12 +100,13 @@ struct RowStats {
   int npos = 0;
   double sum = 0.0;
   float smax = 0.f;
+  // Written without a branch: a score <= 0 adds +0.0 to the sum (which
+  // leaves it unchanged) and cannot raise smax above its start of 0.
   __device__ __forceinline__ void add(float v) {
-    if (v > 0.f) {
-      ++npos;
-      sum += (double)v;
-      smax = fmaxf(smax, v);
-    }
+    const bool pos = v > 0.f;
+    npos += pos;
+    sum += (double)(pos ? v : 0.f);
+    smax = fmaxf(smax, v);
   }
 };
 
