@@ -222,13 +222,16 @@ __device__ __forceinline__ const float* stage_row(const float* g, int n, float* 
   }
 }
 
-// pi_j * 2^32, exactly: pi_of scaled by a power of two (c32 = c * 2^32, and
-// a power-of-two factor commutes with the product's rounding).
-// (Selects rather than branches on the per-block conditions; the mode is the
-// same for the whole row.)
-__device__ __forceinline__ double pi_x32(float s, const PiSolve& ps, double c32) {
-  const double p = (ps.mode == 1 || s >= ps.theta) ? kTwo32 : c32 * (double)s;
-  return ps.mode == 0 ? kTwo32 : (s > 0.f ? p : 0.0);
+// The keep decision of block j (score s, Philox word w): sip_keep(w, x)
+// with x = pi_j * 2^32, which is 2^32 in a mode-0 row and for the certain
+// blocks (mode 1, or s >= theta), 0 for s <= 0, and c32 * s otherwise
+// (exact: c32 = c * 2^32 is pi_of's constant scaled by a power of two,
+// which commutes with the product's rounding).  As w < 2^32, the cases with
+// x = 2^32 keep and the case x = 0 drops without a compare; the rest
+// compares.  Bitwise operators, so that no per-block branch is taken.
+__device__ __forceinline__ bool keep_block(uint32_t w, float s, const PiSolve& ps, double c32) {
+  const bool cert = (ps.mode == 1) | (s >= ps.theta);
+  return (ps.mode == 0) | ((s > 0.f) & (cert | sip_keep(w, c32 * (double)s)));
 }
 
 // Kept-bit mask (4 bits) of blocks 4g..4g+3: one Philox call (counter g),
@@ -251,7 +254,7 @@ __device__ __forceinline__ uint32_t draw_group(const float* s, int n, int g, int
   uint32_t mask = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k)
-    mask |= (uint32_t)((4 * g + k < n) & sip_keep(c[k], pi_x32(v[k], ps, c32))) << k;
+    mask |= (uint32_t)((4 * g + k < n) & keep_block(c[k], v[k], ps, c32)) << k;
   return mask;
 }
 
