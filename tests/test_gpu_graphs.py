@@ -168,3 +168,43 @@ def test_plan_captured_before_side_stream():
     say(r.stdout.strip()[-300:])
     assert r.returncode == 0, r.stderr[-2000:]
     assert "fresh-process capture ok" in r.stdout
+
+
+def test_plans_from_host_threads():
+    """Plan calls from several host threads at once, each on its own stream
+    with its own workspace and plan (the library orders the forks onto its
+    side stream with a lock): every plan equals the sequential one."""
+    import threading
+    wl, (q, k, v) = _inputs(6)
+    prob = lib_problem(wl)
+    budgets = [0.1, 0.15, 0.2, 0.3]
+    refs = [ab.plan(q, k, b, seed=i, problem=prob) for i, b in enumerate(budgets)]
+    torch.cuda.synchronize()
+    outs, errs = {}, []
+
+    def work(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                ws = ab.workspace(prob, q.device)
+                pl = ab.empty_plan(prob, ab.nnz_bound(prob, budgets[i]), q.device)
+                for _ in range(3):
+                    ab.plan(q, k, budgets[i], seed=i, problem=prob, ws=ws, out=pl)
+            st.synchronize()
+            outs[i] = pl
+        except Exception as e:  # reported below, on the main thread
+            errs.append(repr(e))
+
+    ths = [threading.Thread(target=work, args=(i,)) for i in range(len(budgets))]
+    for th in ths:
+        th.start()
+    for th in ths:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errs, errs
+    for i, ref in enumerate(refs):
+        n = ref.nnz()
+        assert torch.equal(outs[i].row_ptr, ref.row_ptr), i
+        assert torch.equal(outs[i].col_idx[:n], ref.col_idx[:n]), i
+        assert torch.equal(outs[i].logw[:n], ref.logw[:n]), i
+    say("host threads: every plan equals the sequential one")
