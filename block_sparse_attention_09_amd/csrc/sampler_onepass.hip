@@ -11,12 +11,12 @@
 // Parallel Prefix Scan with Decoupled Look-back", 2016; rows handed out in
 // ticket order), and writes row_ptr and
 // the ascending block ids with logw = -ln(pi) (float64 log, rounded to fp32;
-// 0 where pi = 1) while its scores are still in LDS, so the score matrix is
-// read once and no scan or fill launch follows.  Forced (text) blocks follow
+// 0 where pi = 1) right away, while its scores are still in the caches, so
+// the score matrix comes from memory once and no scan or fill launch
+// follows.  Forced (text) blocks follow
 // the sampled ones with logw 0.  k_sip_init clears the tickets, the records
 // and the plan status first.
 #include <algorithm>
-#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -93,35 +93,35 @@ __device__ __forceinline__ bool look_back(const uint64_t* flags, int r, uint64_t
   return true;
 }
 
-// One plan row per work-group, rows taken in ticket order: stage the scores
-// (LDS when they fit), solve pi, draw, keep the kept-block bitmask in LDS, find
-// the row's offset in the plan by look-back, then write row_ptr and the
-// row's ids and log-weights (ascending, forced blocks last) straight from LDS.
-// A row whose entries do not fit in the capacity writes nothing; the last row
-// writes row_ptr[R] (the total needed) and the overflow status.
-template <bool kLds>
+// One plan row per work-group, rows taken in ticket order: read the row's
+// scores in place (statistics, solve, draws: the count kernel's code), keep
+// the kept-block bitmask in LDS, find the row's offset in the plan by
+// look-back, then write row_ptr and the row's ids and log-weights (ascending,
+// forced blocks last).  A row whose entries do not fit in the capacity writes
+// nothing; the last row writes row_ptr[R] (the total needed) and the
+// overflow status.
 __global__ __launch_bounds__(kSampT) void k_sip_plan(
     const float* __restrict__ S, int n, int n_forced, int n_qb, int H, int R, double budget,
     uint64_t seed, uint32_t* __restrict__ ticket, uint64_t* __restrict__ flags,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, float* __restrict__ logw,
     int64_t capacity, int32_t* __restrict__ status) {
-  extern __shared__ __align__(16) float dyn[];
+  extern __shared__ __align__(16) uint32_t mask[];  // the row's kept-block bitmask
   __shared__ Red red;
   __shared__ int s_row;
   __shared__ uint64_t s_prefix;
   __shared__ int s_ok;
   __shared__ int wtot[kSampWaves];
+  // kept blocks of one pass over kSampT mask words, as offsets from the
+  // pass's first block (< 32 * kSampT = 16384, so 16 bits suffice)
+  __shared__ uint16_t list[32 * kSampT];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   if (t == 0) s_row = (int)atomicAdd(ticket, 1u);
   __syncthreads();
   const int r = s_row;
   const int qb = r % n_qb, bh = r / n_qb, h = bh % H, b = bh / H;
   const int words = (n + 31) / 32;
-  // dynamic LDS: the scores (kLds, n floats padded to 16 bytes), then the mask
-  float* srow = dyn;
-  uint32_t* mask = reinterpret_cast<uint32_t*>(dyn + (kLds ? ((n + 3) & ~3) : 0));
   RowStats st;
-  const float* s = stage_row<kLds>(S + (int64_t)r * n, n, srow, st);
+  const float* s = stage_row<false>(S + (int64_t)r * n, n, nullptr, st);
   const PiSolve ps = solve_pi(s, n, budget, st, red);
   const double c32 = ps.c * kTwo32;
   const int groups = (n + 3) / 4;
@@ -166,18 +166,18 @@ __global__ __launch_bounds__(kSampT) void k_sip_plan(
   }
   if (!s_ok || (int64_t)prefix + cnt > capacity || (int64_t)prefix + cnt > cap32) return;
 
-  // ids and log-weights of the kept blocks.  First the exclusive prefix of
-  // the kept counts over the mask words (LDS; 16 bits suffice when the row is
-  // staged, n < 65536); then thread t writes kept entries t, t + kSampT, ...:
-  // entry e lies in the last word whose prefix is <= e, at that word's
-  // (e - prefix)-th set bit.  Consecutive entries go to consecutive slots.
-  using Pre = typename std::conditional<kLds, uint16_t, uint32_t>::type;
-  Pre* wpre = reinterpret_cast<Pre*>(mask + words);
+  // ids and log-weights of the kept blocks, kSampT mask words at a time: the
+  // exclusive prefix of the words' kept counts places each thread's word in
+  // an LDS list (ascending), then every thread takes entries i, i + kSampT,
+  // ... of the list, so consecutive entries go to consecutive slots; the
+  // scores of kFillU of them are requested before the first is used
+  constexpr int kFillU = 4;
   const int64_t start = (int64_t)prefix;
   int run = 0;
   for (int base = 0; base < words; base += kSampT) {
     const int wi = base + t;
-    const int k = wi < words ? __popc(mask[wi]) : 0;
+    const uint32_t m = wi < words ? mask[wi] : 0u;
+    const int k = __popc(m);
     int incl = k;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -192,62 +192,41 @@ __global__ __launch_bounds__(kSampT) void k_sip_plan(
       if (q < w) before += wtot[q];
       tot += wtot[q];
     }
-    if (wi < words) wpre[wi] = (Pre)(run + before + incl - k);
+    int pos = before + incl - k;
+    uint32_t mm = m;
+    while (mm) {
+      const int bit = __ffs(mm) - 1;
+      mm &= mm - 1;
+      list[pos++] = (uint16_t)(32 * t + bit);
+    }
+    __syncthreads();
+    const int64_t out = start + run;
+    for (int i0 = t; i0 < tot; i0 += kFillU * kSampT) {
+      int jj[kFillU];
+      float sv[kFillU];
+#pragma unroll
+      for (int u = 0; u < kFillU; ++u) {
+        const int i = i0 + u * kSampT;
+        jj[u] = i < tot ? 32 * base + list[i] : 0;
+        if (i < tot) sv[u] = s[jj[u]];
+      }
+#pragma unroll
+      for (int u = 0; u < kFillU; ++u) {
+        const int i = i0 + u * kSampT;
+        if (i < tot) {
+          const double pi = pi_of(sv[u], ps);
+          col_idx[out + i] = jj[u];
+          logw[out + i] = pi == 1.0 ? 0.0f : (float)(-log(pi));
+        }
+      }
+    }
     run += tot;
     __syncthreads();
-  }
-  for (int e = t; e < run; e += kSampT) {
-    int lo = 0, hi = words - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((int)wpre[mid] <= e) lo = mid;
-      else hi = mid - 1;
-    }
-    uint32_t m = mask[lo];
-    for (int k = e - (int)wpre[lo]; k > 0; --k) m &= m - 1;
-    const int j = 32 * lo + __ffs(m) - 1;
-    const double pi = pi_of(s[j], ps);
-    col_idx[start + e] = j;
-    logw[start + e] = pi == 1.0 ? 0.0f : (float)(-log(pi));
   }
   for (int i = t; i < n_forced; i += kSampT) {
     col_idx[start + run + i] = n + i;
     logw[start + run + i] = 0.0f;
   }
-}
-
-// scores staged in LDS up to 74 KB (18 944 blocks): with the mask words and
-// their 16-bit prefixes two work-groups still fit on a CU (158.3 KB at
-// 18 900 blocks); longer rows are read from L2 (as in the count kernel of
-// the three-kernel sampler)
-constexpr size_t kOnePassLdsMax = 74 * 1024;
-
-template <bool kLds>
-static hipError_t launch_onepass_t(const Shape& s, const float* S, double budget, uint64_t seed,
-                                   void* ws, int32_t* row_ptr, int32_t* col_idx, float* logw,
-                                   int64_t capacity, int32_t* status, hipStream_t st) {
-  // LDS: the scores (staged rows; padded to 16 bytes), the mask words and
-  // their prefixes (16-bit for staged rows, padded to 4 bytes)
-  const size_t words = (size_t)(s.n_kbs + 31) / 32;
-  const size_t lds = (kLds ? (size_t)((s.n_kbs + 3) & ~3) * sizeof(float) : 0) +
-                     words * sizeof(uint32_t) +
-                     (kLds ? (words * 2 + 3) / 4 * 4 : words * sizeof(uint32_t));
-  const int n_forced = s.n_kb - s.n_kbs;
-  const OnePassWs l = onepass_ws_layout(s);
-  char* base = static_cast<char*>(ws);
-  uint32_t* ticket = reinterpret_cast<uint32_t*>(base + l.ticket);
-  uint64_t* flags = reinterpret_cast<uint64_t*>(base + l.flags);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_sip_plan<kLds>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  const int init_blocks = (int)std::min<int64_t>(((int64_t)s.R + 255) / 256, 1024);
-  k_sip_init<<<init_blocks, 256, 0, st>>>(ticket, flags, s.R, status);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  k_sip_plan<kLds><<<s.R, kSampT, lds, st>>>(S, s.n_kbs, n_forced, s.n_qb, s.H, s.R, budget,
-                                             seed, ticket, flags, row_ptr, col_idx, logw,
-                                             capacity, status);
-  return hipGetLastError();
 }
 
 OnePassWs onepass_ws_layout(const Shape& s) {
@@ -262,11 +241,24 @@ OnePassWs onepass_ws_layout(const Shape& s) {
 hipError_t launch_sampler_onepass(const Shape& s, const float* S, double budget, uint64_t seed,
                                   void* ws, int32_t* row_ptr, int32_t* col_idx, float* logw,
                                   int64_t capacity, int32_t* status, hipStream_t st) {
-  if ((size_t)s.n_kbs * sizeof(float) <= kOnePassLdsMax)
-    return launch_onepass_t<true>(s, S, budget, seed, ws, row_ptr, col_idx, logw, capacity,
-                                  status, st);
-  return launch_onepass_t<false>(s, S, budget, seed, ws, row_ptr, col_idx, logw, capacity,
-                                 status, st);
+  // dynamic LDS: the mask words (2.4 KB at 18 900 blocks); with the 32 KB
+  // list, four work-groups share a CU
+  const size_t lds = (size_t)(s.n_kbs + 31) / 32 * sizeof(uint32_t);
+  const int n_forced = s.n_kb - s.n_kbs;
+  const OnePassWs l = onepass_ws_layout(s);
+  char* base = static_cast<char*>(ws);
+  uint32_t* ticket = reinterpret_cast<uint32_t*>(base + l.ticket);
+  uint64_t* flags = reinterpret_cast<uint64_t*>(base + l.flags);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_sip_plan),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int init_blocks = (int)std::min<int64_t>(((int64_t)s.R + 255) / 256, 1024);
+  k_sip_init<<<init_blocks, 256, 0, st>>>(ticket, flags, s.R, status);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_sip_plan<<<s.R, kSampT, lds, st>>>(S, s.n_kbs, n_forced, s.n_qb, s.H, s.R, budget, seed,
+                                       ticket, flags, row_ptr, col_idx, logw, capacity, status);
+  return hipGetLastError();
 }
 
 }  // namespace abatt
