@@ -177,12 +177,11 @@ abatt_status abatt_plan(const abatt_problem_t *p, const void *Q, const void *K,
  * abatt_plan: the same scores, pi and draws.  One work-group per plan row,
  * rows taken in ticket order, solves pi, draws, finds the row's offset in
  * the plan from the counts of the rows before it (decoupled look-back over
- * one 64-bit record per row) and writes the row from LDS, so no scan or fill
- * launch follows and the score matrix is read once.  On MI355X it is slower
- * than abatt_plan where score rows fit in LDS (about 2% at 18 900 key blocks:
- * the draw phase keeps its kept-block masks in LDS and runs at fewer waves
- * per CU) and equal where they are read from memory (29 700 blocks); it is
- * kept for that comparison.
+ * one 64-bit record per row) and writes the row at once, so no scan or fill
+ * launch follows and the score matrix comes from memory once.  On MI355X it
+ * is slower than abatt_plan at 18 900 key blocks (1-4% of the plan: its one
+ * kernel takes longer than count, scan and fill together) and about equal at
+ * 29 700; it is kept for that comparison.
  *   - The look-back waits only for rows that took their tickets earlier, so
  *     it always ends; its spin is bounded all the same, and a plan whose
  *     look-back hit the bound gets *status = 2 (invalid, like an overflow).

@@ -2,9 +2,11 @@
 tickets and chained by decoupled look-back) against abatt_plan (three
 kernels), through the binding: the same plan bit for bit -- status, row_ptr,
 col_idx and the bits of logw -- on small and ragged shapes, text tokens,
-key-block sizes from 4 to 128, budget 1, rows on both sides of the length
-that still stages in LDS, and a capacity overflow (same status, same row_ptr).  One small case also checks the
-one-pass plan against the oracle's (block agreement, as for abatt_plan)."""
+key-block sizes from 4 to 128, budget 1, long rows (18 944 to 40 000 key
+blocks, with the mask words of a pass up to the LDS list's limit), many rows
+(long look-back chains) and a capacity overflow (same status, same row_ptr).
+One small case also checks the one-pass plan against the oracle's (block
+agreement, as for abatt_plan)."""
 import numpy as np
 import pytest
 import torch
@@ -27,12 +29,11 @@ CASES = {
     "bf16_kv128_text": (Workload("k128", B=1, H=1, D=64, grid=(4, 16, 16), n_text=128,
                                  kv_block=128), 0.5),
     "bf16_all": (Workload("m", B=1, H=2, D=128, grid=(6, 16, 24)), 1.0),
-    # 18 944 key blocks: the longest rows whose scores the one-pass kernel stages in
-    # LDS (74 KB); the three-kernel count kernel reads every row in place
-    "bf16_row_staged": (Workload("L", B=1, H=1, D=64, grid=(1, 4, 18944)), 0.1),
-    # 18 948 key blocks: the one-pass kernel reads them from the workspace instead
-    "bf16_row_past_stage": (Workload("P", B=1, H=1, D=64, grid=(1, 4, 18948)), 0.1),
-    # 40 000 key blocks: both samplers read the rows from the workspace
+    # long rows, read in place by both samplers: 18 944 and 18 948 key blocks
+    # (two passes of the LDS list, the second one short)
+    "bf16_row_18944": (Workload("L", B=1, H=1, D=64, grid=(1, 4, 18944)), 0.1),
+    "bf16_row_18948": (Workload("P", B=1, H=1, D=64, grid=(1, 4, 18948)), 0.1),
+    # 40 000 key blocks: 1250 mask words, three passes of the LDS list
     "bf16_row_global": (Workload("G", B=1, H=1, D=64, grid=(20, 40, 200)), 0.1),
     # many rows (12 heads x 256 query blocks): look-back over long chains
     "bf16_many_rows": (Workload("M", B=1, H=12, D=64, grid=(8, 64, 64)), 0.08),
