@@ -123,19 +123,21 @@ constexpr int kMaxDevices = 64;
 std::mutex g_side_mu;
 Side g_side[kMaxDevices];
 
-// The current device's side stream, created on first use; nullptr when there
-// is none to be had: creation failed, the device index is out of range, or
-// it does not exist yet and may not be created now (`may_create` false, or
-// `stream` under capture).  Called with g_side_mu held.
+// The current device's side stream, created on first use; nullptr when it is
+// not to be used: `stream` is under capture (a stream that joins a capture
+// stays part of it until the capture ends, so eager calls from other threads
+// would be captured too; captured plans run on `stream` alone), the device
+// index is out of range, creation failed, or the stream does not exist yet
+// and may not be created (`may_create` false).  Called with g_side_mu held.
 Side* side_stream(hipStream_t stream, bool may_create) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+    return nullptr;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
   Side& sd = g_side[dev];
   if (sd.s != nullptr) return &sd;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (!may_create || hipStreamIsCapturing(stream, &cs) != hipSuccess ||
-      cs != hipStreamCaptureStatusNone)
-    return nullptr;
+  if (!may_create) return nullptr;
   Side n;
   if (hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) == hipSuccess &&
       hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) == hipSuccess &&
@@ -158,9 +160,9 @@ Side* side_stream(hipStream_t stream, bool may_create) {
 // latency of its Lloyd iterations) do not depend on each other, so they run
 // side by side: the key means on the side stream, forked from `stream` by an
 // event, k-means on `stream`, which waits for the side stream's join event
-// before the scorer.  The call thus stays ordered on `stream` and can be
-// captured into a graph.  Without a side stream both run on `stream`, one
-// after the other (the same results).
+// before the scorer.  The call thus stays ordered on `stream`.  Without a
+// side stream (and always under graph capture) both run on `stream`, one
+// after the other, with the same results.
 hipError_t run_scores(const Shape& s, const PlanWs& l, char* ws, const void* Q, const void* K,
                       float* mu, float* w, float* S, hipStream_t stream, bool may_create = true) {
   uint16_t* kplanes = reinterpret_cast<uint16_t*>(ws + l.kmean);

@@ -36,10 +36,11 @@
  *     stream that the library creates once per device (default priority,
  *     kept until the process ends).  It is forked from `stream` by an event
  *     and joined back by another before the scorer, so the call's work stays
- *     ordered on `stream` and a graph captured from `stream` holds both
- *     branches.  The side stream is never created while `stream` is under
- *     capture, nor by abatt_plan_noalloc: without it both kernels run on
- *     `stream`, with the same results.
+ *     ordered on `stream`.  While `stream` is under graph capture the side
+ *     stream is not used (a stream that joins a capture stays in it until
+ *     the capture ends, and would pull other threads' calls in): both
+ *     kernels then run on `stream`, one after the other, with the same
+ *     results.  abatt_plan_noalloc never creates the side stream.
  *   - Invalid arguments are reported synchronously, before any HIP call, as a
  *     negative abatt_status; nothing is enqueued then.  A failed launch gives
  *     ABATT_EHIP.  Device-side conditions (a plan that outgrew its capacity)

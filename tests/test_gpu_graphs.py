@@ -1,9 +1,9 @@
 """The library under HIP graph capture and on concurrent streams.
 
 Every entry point only enqueues kernels on the caller's stream (no memsets,
-copies, allocations or synchronisations; the plan's key means run on the
-library's side stream, forked from the caller's stream and joined back to
-it), so a plan + attend sequence (also with the V conversion of the fp16-V
+copies, allocations or synchronisations; outside capture the plan's key
+means run on the library's side stream, forked from the caller's stream and
+joined back to it), so a plan + attend sequence (also with the V conversion of the fp16-V
 form) can be captured once and replayed, and calls on different streams with
 their own workspaces and plans do not interfere.  Checked bit for bit against eager
 calls: several replays with eager work and synchronisations between them, and
@@ -134,7 +134,7 @@ torch.cuda.synchronize()
 ws = ab.workspace(prob, q.device)
 pl = ab.empty_plan(prob, ab.nnz_bound(prob, budget), q.device)
 g = torch.cuda.CUDAGraph()
-with torch.cuda.graph(g):  # no side stream yet: the captured plan runs on one stream
+with torch.cuda.graph(g):  # under capture the plan runs on the captured stream alone
     ab.plan(q, k, budget, seed=seed, problem=prob, ws=ws, out=pl)
 g.replay()
 torch.cuda.synchronize()
@@ -153,9 +153,9 @@ print("fresh-process capture ok", n)
 
 
 def test_plan_captured_before_side_stream():
-    """A plan captured before the library has its side stream (the first plan
-    call of a process, under capture) runs on the captured stream alone; its
-    replays equal eager plans made afterwards with the side stream."""
+    """A plan captured as the first plan call of a process, before the library
+    has made its side stream (captured plans never use it): its replays
+    equal eager plans made afterwards, with the side stream."""
     import os
     import subprocess
     import sys
@@ -208,3 +208,48 @@ def test_plans_from_host_threads():
         assert torch.equal(outs[i].col_idx[:n], ref.col_idx[:n]), i
         assert torch.equal(outs[i].logw[:n], ref.logw[:n]), i
     say("host threads: every plan equals the sequential one")
+
+
+def test_eager_plans_beside_a_capture():
+    """One thread captures a plan while another runs eager plans on its own
+    stream: captured plans never touch the side stream, so the eager plans
+    run (and come out right) and the graph replays the captured plan."""
+    import threading
+    wl, (q, k, v) = _inputs(7)
+    prob = lib_problem(wl)
+    ref_a = ab.plan(q, k, 0.15, seed=3, problem=prob)
+    ref_b = ab.plan(q, k, 0.2, seed=4, problem=prob)
+    torch.cuda.synchronize()
+    ws_a, ws_b = ab.workspace(prob, q.device), ab.workspace(prob, q.device)
+    pl_a = ab.empty_plan(prob, ab.nnz_bound(prob, 0.15), q.device)
+    pl_b = ab.empty_plan(prob, ab.nnz_bound(prob, 0.2), q.device)
+    sb = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    errs = []
+
+    def other():
+        try:
+            with torch.cuda.stream(sb):
+                for _ in range(3):
+                    ab.plan(q, k, 0.2, seed=4, problem=prob, ws=ws_b, out=pl_b)
+            sb.synchronize()
+        except Exception as e:  # reported below, on the main thread
+            errs.append(repr(e))
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="thread_local"):
+        th = threading.Thread(target=other)
+        th.start()
+        ab.plan(q, k, 0.15, seed=3, problem=prob, ws=ws_a, out=pl_a)
+        th.join()
+    assert not errs, errs
+    for rep in range(2):
+        pl_a.col_idx.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        for pl, ref in ((pl_a, ref_a), (pl_b, ref_b)):
+            n = ref.nnz()
+            assert torch.equal(pl.row_ptr, ref.row_ptr), rep
+            assert torch.equal(pl.col_idx[:n], ref.col_idx[:n]), rep
+            assert torch.equal(pl.logw[:n], ref.logw[:n]), rep
+    say("eager plans beside a capture: both right")
