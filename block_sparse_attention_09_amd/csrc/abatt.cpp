@@ -131,8 +131,11 @@ Side g_side[kMaxDevices];
 // and may not be created (`may_create` false).  Called with g_side_mu held.
 Side* side_stream(hipStream_t stream, bool may_create) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    (void)hipGetLastError();  // the launches that follow report their own errors
     return nullptr;
+  }
+  if (cs != hipStreamCaptureStatusNone) return nullptr;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
   Side& sd = g_side[dev];
@@ -184,8 +187,8 @@ hipError_t run_scores(const Shape& s, const PlanWs& l, char* ws, const void* Q, 
       e = hipEventRecord(sd->fork, stream);
       if (e == hipSuccess) e = hipStreamWaitEvent(sd->s, sd->fork, 0);
       if (e == hipSuccess) {
-        // joined whatever the launches return, so that the side stream never
-        // stays forked off a capture
+        // joined whatever the launches return: `stream` always waits for
+        // the side stream's work before it goes on
         const hipError_t ek = key_means(sd->s);
         const hipError_t er = hipEventRecord(sd->join, sd->s);
         const hipError_t em = abatt::launch_kmeans(s, Q, mu, w, stream);
