@@ -139,9 +139,12 @@ __global__ __launch_bounds__(256) void k_key_means_f32(const float* __restrict__
 // bf16 input, the scoring form for bf16 problems: the means of one tile of
 // 32 consecutive blocks of a head (the scorer's tile) as fp16 values scaled
 // by 2^-e, with e chosen so that the tile's largest magnitude lands in
-// [2^14, 2^15), and 2^e in tscale[head tile].  A power-of-two scale is exact,
-// so every mean keeps fp16's 11 significant bits whatever the keys' range (no
-// overflow; underflow only for values 2^-28 below the tile's largest).
+// [1, 2), and 2^e in tscale[head tile] (2^-126 for a tile of zeros).  A
+// power-of-two scale is exact, so every mean keeps fp16's 11 significant bits
+// whatever the keys' range (no overflow; below fp16's normal range only for
+// values 2^-14 below the tile's largest).  The scorer rescales whole tiles by
+// powers of two on their way to LDS, which a largest value near 1 leaves
+// room for in both directions.
 // One work-group per (head, tile); a thread holds 8 dims of 1 (D = 64) or 2
 // (D = 128) blocks, reduces the tile's largest |mean| with the others, then
 // scales, rounds to nearest and stores.
@@ -176,8 +179,8 @@ __global__ __launch_bounds__(256) void k_key_means_f16(const uint16_t* __restric
   if ((t & 63) == 0) red[t >> 6] = amax;
   __syncthreads();
   const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  // m = f * 2^x with f in [0.5, 1): m * 2^-(x - 15) lies in [2^14, 2^15)
-  int e = m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 15 : 0;
+  // m = f * 2^x with f in [0.5, 1): m * 2^-(x - 1) lies in [1, 2)
+  int e = m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 1 : -126;
   e = e < -126 ? -126 : (e > 127 ? 127 : e);
 #pragma unroll
   for (int ii = 0; ii < NI; ++ii) {

@@ -34,6 +34,8 @@
 // Each pass is software-pipelined: the MFMAs of tile t+1 are issued in the
 // same block as the exp2 work of tile t, so the matrix core and the vector
 // ALU run side by side.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
   constexpr int NP = kF16 ? 1 : 2;                         // planes of key means
   __shared__ __align__(16) uint16_t ring[kScoreStages][NP][32 * ROWB];
   __shared__ float tsc[kScoreStages];  // scale of the tile in each stage (kF16)
-  __shared__ float red[kScoreWaves];
+  __shared__ float red[3 * kScoreWaves];
   __shared__ float a_lds[ROWS];
 
   // work-group -> (group, split): consecutive work-groups (one XCD) take
@@ -119,7 +121,12 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
   // runs in the half-iteration of tile t (stage (t+1)%3 was stored before the
   // previous barrier, and stage (t+2)%3 was last read one half-iteration
   // earlier still).
-  auto run_pass = [&](const uint16_t* p0, const uint16_t* p1, auto&& mma, auto&& fix, auto&& epi) {
+  // unit scale (below): key means times 2^-a_shift, centroids times 2^a_shift
+  int a_shift = 0;
+  bool unit = false;
+  auto run_pass = [&](const uint16_t* p0, const uint16_t* p1, auto&& mma, auto&& fix, auto&& epi,
+                      auto unit_tag) {
+    constexpr bool kU = decltype(unit_tag)::value;
     struct Regs {
       u32x4 v[NP][NCH];
       float sc;
@@ -140,16 +147,26 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
       if constexpr (kF16) r.sc = tsbase[tile];
     };
     auto store_tile = [&](const Regs& r, int stage) {
+      // unit scale: the tile's means times 2^-a_shift, i.e. its scale 2^e
+      // times 2^-a_shift as one fp16 factor (a normal power of two for every
+      // tile but zero tiles, whose factor rounds to 0): exact products
+      _Float16 f = (_Float16)1.f;
+      if constexpr (kU) f = (_Float16)__builtin_amdgcn_ldexpf(r.sc, -a_shift);
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
         const int q = i * kScoreT + t;
         if (q < TILE_CH) {
           const int o = (q / CH) * ROWB + 8 * (q % CH);
-#pragma unroll
-          for (int pl = 0; pl < NP; ++pl) *reinterpret_cast<u32x4*>(&ring[stage][pl][o]) = r.v[pl][i];
+          u32x4 v0 = r.v[0][i];
+          if constexpr (kU) {
+            const f16x8 h = __builtin_bit_cast(f16x8, v0);
+            v0 = __builtin_bit_cast(u32x4, h * f);
+          }
+          *reinterpret_cast<u32x4*>(&ring[stage][0][o]) = v0;
+          if constexpr (NP == 2) *reinterpret_cast<u32x4*>(&ring[stage][1][o]) = r.v[1][i];
         }
       }
-      if constexpr (kF16)
+      if constexpr (kF16 && !kU)
         if (t == 0) tsc[stage] = r.sc;
     };
     load_tile(ra, t_begin);
@@ -164,20 +181,21 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
     auto nxt = [](int s) { return s == kScoreStages - 1 ? 0 : s + 1; };
     // Each half-iteration's MFMAs and exp2 work form one branch-free block;
     // the MFMAs past the last tile read a stale stage and are discarded.
+    // `epi` also sees the next tile's logits, issued before it runs.
     for (int tile = t_begin; tile < t_end; tile += 2) {
       const int s1 = nxt(st), s2 = nxt(s1);
       store_tile(ra, s2);
       load_tile(ra, min(tile + 4, tlast));
       fix(xa, tile);
       xb = mma(s1);
-      epi(xa, tile, st);
+      epi(xa, xb, tile, st);
       __syncthreads();
       if (tile + 1 < t_end) {
         store_tile(rb, st);  // stage of tile + 3
         load_tile(rb, min(tile + 5, tlast));
         fix(xb, tile + 1);
         xa = mma(s2);
-        epi(xb, tile + 1, s1);
+        epi(xb, xa, tile + 1, s1);
         __syncthreads();
       }
       st = s2;
@@ -185,11 +203,21 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
   };
 
   // centroid operands: bf16 hi/lo (fp32 problems) or fp16 scaled by 2^-e_mu
-  // (bf16 problems; e_mu from the work-group's largest |scale_log2 * mu|)
+  // (bf16 problems)
   constexpr int KH = kF16 ? 1 : KS;
   bf16x8 mh[KH], ml[KH];
   f16x8 m16[kF16 ? KS : 1];
   float fac_mu = 1.f;  // 2^e_mu
+  // Unit scale (bf16 problems).  When the work-group's largest |scale_log2 *
+  // mu| (2^em bounds it) and largest |key mean| (2^kk bounds it, from the
+  // largest tile scale) allow it, the centroids are scaled by 2^a and the key
+  // means by 2^-a, a = floor((kk - em) / 2), so both largest magnitudes lie
+  // in [2^-4, 2^14] and every tile's factor 2^(e - a) is a normal fp16.  The
+  // MFMA then yields the logit itself (log2 units), and the offset each pass
+  // subtracts or adds rides in the accumulator input instead of one fma per
+  // logit.  Otherwise (logits beyond 2^28, near-zero logits, or tiles whose
+  // scales span more than about 2^13) the tile-scale factor is applied per
+  // logit as before.
   if constexpr (kF16) {
     float x[KS][8];
     float amax = 0.f;
@@ -199,14 +227,45 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
 #pragma unroll
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[s][i]));
     }
+    // largest and smallest scale of this work-group's tiles (zero tiles,
+    // scale 2^-126, left out)
+    float smax = 0.f, smin = INFINITY;
+    for (int i = t_begin + t; i < t_end; i += kScoreT) {
+      const float sc = tsbase[i];
+      if (sc > 0x1p-126f) {
+        smax = fmaxf(smax, sc);
+        smin = fminf(smin, sc);
+      }
+    }
     amax = wave_max(amax);
-    if (lane == 0) red[wv] = amax;
+    smax = wave_max(smax);
+    smin = wave_min(smin);
+    if (lane == 0) {
+      red[wv] = amax;
+      red[kScoreWaves + wv] = smax;
+      red[2 * kScoreWaves + wv] = smin;
+    }
     __syncthreads();
-    float m = red[0];
+    float m = red[0], sM = red[kScoreWaves], sm = red[2 * kScoreWaves];
 #pragma unroll
-    for (int i = 1; i < kScoreWaves; ++i) m = fmaxf(m, red[i]);
+    for (int i = 1; i < kScoreWaves; ++i) {
+      m = fmaxf(m, red[i]);
+      sM = fmaxf(sM, red[kScoreWaves + i]);
+      sm = fminf(sm, red[2 * kScoreWaves + i]);
+    }
     // m = f * 2^x with f in [0.5, 1): m * 2^-(x - 15) lies in [2^14, 2^15)
     int e = m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 15 : 0;
+    if (m > 0.f && sM > 0.f) {
+      const int em = __builtin_amdgcn_frexp_expf(m);    // m < 2^em
+      const int kk = __builtin_amdgcn_frexp_expf(sM);   // |key mean| < 2 sM = 2^kk
+      const int a = (kk - em) >> 1;
+      const int lo_f = __builtin_amdgcn_frexp_expf(sm) - 1 - a;  // log2 of the smallest factor
+      if (em + a >= -3 && em + a <= 14 && kk - a >= -3 && kk - a <= 14 && lo_f >= -14) {
+        unit = true;
+        a_shift = a;
+        e = -a;
+      }
+    }
     e = e < -126 ? -126 : (e > 127 ? 127 : e);
     fac_mu = __builtin_amdgcn_ldexpf(1.f, e);
 #pragma unroll
@@ -229,13 +288,26 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
 
   // ---------------- pass 1: softmax normaliser of every centroid ----------------
   float m_run = -INFINITY, s_run = 0.f;
-  if constexpr (kMode != 2) {
+  // kU: the logits come straight from the MFMAs and each term is just
+  // exp2(logit), summed against 0 and carried to the reference (which starts
+  // at 0) once per tile; an underflowed sum sends the work-group to the
+  // general form below
+  auto pass1 = [&](auto unit_tag) {
+    constexpr bool kU = decltype(unit_tag)::value;
+    m_run = kU ? 0.f : -INFINITY;
+    s_run = 0.f;
+    float r_ref = 1.f;  // kU: 2^-m_run
     auto mma1 = [&](int stage) {
       f32x16 x = {};
       if constexpr (kF16) {
 #pragma unroll
         for (int s = 0; s < KS; ++s)
           x = mfma_f16_32x32x16(__builtin_bit_cast(f16x8, kop(ring[stage][0], s)), m16[s], x);
+        if constexpr (kU) {
+          // every operand read of the tile ahead of its MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
+        }
       } else {
         // one accumulation chain: the small cross terms first, then hi*hi
 #pragma unroll
@@ -260,7 +332,35 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
           if (32 * tile + 8 * (v >> 2) + 4 * hh + (v & 3) >= n_kbs) x[v] = -INFINITY;
       }
     };
-    auto epi1 = [&](const f32x16& x, int, int stage) {
+    auto epi1 = [&](const f32x16& x, f32x16&, int, int stage) {
+      if constexpr (kU) {
+        // the tile's sum against 0, carried to the reference by one product
+        float ps = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ps += __builtin_amdgcn_exp2f(x[v]);
+        // above 2^60 on any lane (or inf): move the reference to the running
+        // max and sum the tile against it (every tile does this while the
+        // logits stay above about 60)
+        if (__builtin_expect(__any(__float_as_uint(ps) > 0x5d800000u), 0)) {
+          f32x16 xs = x;
+          asm volatile("" : "+v"(xs));
+          float tmax = -INFINITY;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, xs[v]);
+          const f32x2 tp = pair_x32(tmax);
+          const float m_new = fmaxf(m_run, fmaxf(tp[0], tp[1]));
+          s_run *= __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          r_ref = __builtin_amdgcn_exp2f(-m_run);
+          ps = 0.f;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) ps += __builtin_amdgcn_exp2f(xs[v] - m_run);
+          s_run += ps;
+        } else {
+          s_run = fmaf(ps, r_ref, s_run);
+        }
+        return;
+      }
       // logit = fac * x, fac a positive power of two (1 for split operands)
       const float fac = kF16 ? tsc[stage] * fac_mu : 1.f;
       auto tile_sum = [&]() {
@@ -289,9 +389,23 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
       }
       s_run += ps;
     };
-    run_pass(hbase, lbase, mma1, fix1, epi1);
+    run_pass(hbase, lbase, mma1, fix1, epi1, unit_tag);
     const f32x2 sp = pair_x32(s_run);
     s_run = sp[0] + sp[1];
+  };
+  if constexpr (kMode != 2) {
+    if constexpr (kF16) {
+      if (unit) {
+        pass1(std::true_type{});
+        // every logit of a centroid far below the starting reference (its sum
+        // underflowed): the work-group takes the general form of pass 1
+        if (__syncthreads_or(rvalid && !(s_run >= 0x1p-60f))) pass1(std::false_type{});
+      } else {
+        pass1(std::false_type{});
+      }
+    } else {
+      pass1(std::false_type{});
+    }
   }
   if constexpr (kMode == 1) {
     // this split's partial normaliser of every centroid row: the sum of
@@ -319,7 +433,7 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
   __syncthreads();
 
   // ---------------- pass 2: weighted probabilities summed per query block ----------------
-  float a_v[16];
+  f32x16 a_v;
 #pragma unroll
   for (int v = 0; v < 16; ++v) a_v[v] = a_lds[32 * wv + 8 * (v >> 2) + 4 * hh + (v & 3)];
   // S rows of this work-group's query blocks through a bounds-checked buffer:
@@ -332,62 +446,80 @@ __global__ __launch_bounds__(kScoreT, 1) void k_scores(const float* __restrict__
     const uint32_t off = key < n_kbs ? (uint32_t)(qrel * n_kbs + key) * 4u : 0x80000000u;
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), srs, off, 0, 0);
   };
-  auto mma2 = [&](int stage) {
-    f32x16 x = {};
-    if constexpr (kF16) {
+  // kU: the MFMAs start from the centroid offsets, so their result is the
+  // exponent itself
+  auto pass2 = [&](auto unit_tag) {
+    constexpr bool kU = decltype(unit_tag)::value;
+    auto mma2 = [&](int stage) {
+      f32x16 x = kU ? a_v : f32x16{};
+      if constexpr (kF16) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        x = mfma_f16_32x32x16(m16[s], __builtin_bit_cast(f16x8, kop(ring[stage][0], s)), x);
-    } else {
-      // one accumulation chain: the small cross terms first, then hi*hi
+        for (int s = 0; s < KS; ++s)
+          x = mfma_f16_32x32x16(m16[s], __builtin_bit_cast(f16x8, kop(ring[stage][0], s)), x);
+        if constexpr (kU) {
+          __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
+        }
+      } else {
+        // one accumulation chain: the small cross terms first, then hi*hi
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 kh = __builtin_bit_cast(bf16x8, kop(ring[stage][0], s));
-        const bf16x8 kl = __builtin_bit_cast(bf16x8, kop(ring[stage][NP - 1], s));
-        x = mfma_bf16_32x32x16(mh[s], kl, x);
-        x = mfma_bf16_32x32x16(ml[s], kh, x);
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 kh = __builtin_bit_cast(bf16x8, kop(ring[stage][0], s));
+          const bf16x8 kl = __builtin_bit_cast(bf16x8, kop(ring[stage][NP - 1], s));
+          x = mfma_bf16_32x32x16(mh[s], kl, x);
+          x = mfma_bf16_32x32x16(ml[s], kh, x);
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          x = mfma_bf16_32x32x16(mh[s], __builtin_bit_cast(bf16x8, kop(ring[stage][0], s)), x);
       }
+      return x;
+    };
+    auto fix2 = [](f32x16&, int) {};
+    auto epi2 = [&](const f32x16& x, f32x16&, int tile, int stage) {
+      // lane: key 32*tile + l32, centroid rows 32*wv + 8*(v/4) + 4*hh + v%4
+      const float fac = (kF16 && !kU) ? tsc[stage] * fac_mu : 1.f;
+      float p[16];
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        x = mfma_bf16_32x32x16(mh[s], __builtin_bit_cast(bf16x8, kop(ring[stage][0], s)), x);
-    }
-    return x;
+      for (int v = 0; v < 16; ++v)
+        p[v] = __builtin_amdgcn_exp2f(kU ? x[v] : fmaf(x[v], fac, a_v[v]));
+      const int key = 32 * tile + l32;
+      if constexpr (C == 8) {
+        // rows 8g..8g+7 of the wave = one query block; this half holds 4 of them
+        float part[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          part[g] = (p[4 * g] + p[4 * g + 1]) + (p[4 * g + 2] + p[4 * g + 3]);
+        // the lower half completes blocks 2 and 3, the upper half blocks 0 and 1
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const f32x2 r = cross_x32(part[2 + gg], part[gg]);
+          put(4 * wv + (hh ? gg : 2 + gg), key, r[0] + r[1]);
+        }
+      } else {
+        // C == 16: rows 16gp..16gp+15 = one query block
+        float part[2];
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          part[gp] = 0.f;
+#pragma unroll
+          for (int v = 8 * gp; v < 8 * gp + 8; ++v) part[gp] += p[v];
+        }
+        // the lower half completes block 1, the upper half block 0
+        const f32x2 r = cross_x32(part[1], part[0]);
+        put(2 * wv + (hh ? 0 : 1), key, r[0] + r[1]);
+      }
+    };
+    run_pass(hbase, lbase, mma2, fix2, epi2, unit_tag);
   };
-  auto fix2 = [](f32x16&, int) {};
-  auto epi2 = [&](const f32x16& x, int tile, int stage) {
-    // lane: key 32*tile + l32, centroid rows 32*wv + 8*(v/4) + 4*hh + v%4
-    const float fac = kF16 ? tsc[stage] * fac_mu : 1.f;
-    float p[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(x[v], fac, a_v[v]));
-    const int key = 32 * tile + l32;
-    if constexpr (C == 8) {
-      // rows 8g..8g+7 of the wave = one query block; this half holds 4 of them
-      float part[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        part[g] = (p[4 * g] + p[4 * g + 1]) + (p[4 * g + 2] + p[4 * g + 3]);
-      // the lower half completes blocks 2 and 3, the upper half blocks 0 and 1
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const f32x2 r = cross_x32(part[2 + gg], part[gg]);
-        put(4 * wv + (hh ? gg : 2 + gg), key, r[0] + r[1]);
-      }
-    } else {
-      // C == 16: rows 16gp..16gp+15 = one query block
-      float part[2];
-#pragma unroll
-      for (int gp = 0; gp < 2; ++gp) {
-        part[gp] = 0.f;
-#pragma unroll
-        for (int v = 8 * gp; v < 8 * gp + 8; ++v) part[gp] += p[v];
-      }
-      // the lower half completes block 1, the upper half block 0
-      const f32x2 r = cross_x32(part[1], part[0]);
-      put(2 * wv + (hh ? 0 : 1), key, r[0] + r[1]);
-    }
-  };
-  run_pass(hbase, lbase, mma2, fix2, epi2);
+  if constexpr (kF16) {
+    if (unit)
+      pass2(std::true_type{});
+    else
+      pass2(std::false_type{});
+  } else {
+    pass2(std::false_type{});
+  }
 }
 
 // Splits of each group's tiles: the fewest that fill the rounds of work-

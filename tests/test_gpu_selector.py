@@ -18,7 +18,7 @@ import torch
 import oracle
 from helpers import (jaccard, lib_problem, oracle_problem, plan_to_host, say, to_dev,
                      ulp_diff_f32)
-from workloads import CONFIGS, Workload, make_qkv, random_scores
+from workloads import CONFIGS, Workload, make_qkv, random_scores, round_like
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +51,7 @@ def test_key_means_scoring_form(name):
     plane [B,H,n_kbs,D] at the start of the plan workspace, followed by one fp32
     scale 2^e per tile of 32 blocks of a head.  plane * scale must be the mean
     to fp16's rounding: 2^-11 relative, plus half an fp16 subnormal step (2^-25
-    in plane units) for values 2^-28 below their tile's largest."""
+    in plane units) for values 2^-14 below their tile's largest."""
     wl = SEL[name]
     q, k, v = make_qkv(wl)
     op = oracle_problem(wl)
@@ -72,7 +72,7 @@ def test_key_means_scoring_form(name):
     plane = plane.reshape(prob.B, prob.H, prob.n_kbs, prob.D)
     scale = raw[2 * n_plane:2 * n_plane + 4 * prob.B * prob.H * n_tiles].view(np.float32)
     scale = scale.astype(np.float64).reshape(prob.B, prob.H, n_tiles)
-    # scales are powers of two that put each tile's largest |mean| in [2^14, 2^15)
+    # scales are powers of two that put each tile's largest |mean| in [1, 2)
     assert np.all(np.log2(scale) == np.round(np.log2(scale)))
     tile = np.repeat(scale, 32, axis=2)[:, :, :prob.n_kbs, None]
     got = plane * tile
@@ -80,7 +80,7 @@ def test_key_means_scoring_form(name):
     bound = 2.0 ** -11 * np.abs(ref) + 2.0 ** -25 * tile + 1e-30
     say(f"  max error / bound {np.max(err / bound):.3f}, max rel {np.max(err / np.maximum(np.abs(ref), 1e-30)):.2e}")
     assert np.all(err <= bound)
-    assert np.abs(plane).max() < 2.0 ** 15
+    assert np.abs(plane).max() < 2.0
 
 
 @pytest.mark.parametrize("name", list(SEL))
@@ -121,6 +121,46 @@ def test_scores_invariant_under_power_of_two_key_scaling(name, k2):
                          lib_problem(wl, scale=float(np.ldexp(s0, -k2))))
     torch.cuda.synchronize()
     assert torch.equal(S0, S1)
+
+
+# Inputs that send the bf16 scorer off its unit scale (where the fp16 MFMA
+# yields the logits themselves and the pass offsets ride in the accumulator
+# input) onto the per-logit tile-scale form: every logit below -100 (log2 units,
+# so pass 1's sums underflow against the starting reference 0 and the
+# work-group redoes pass 1 with a moving reference), one tile of keys 2^20
+# smaller than the rest (tile scales too far apart for one fp16 factor each),
+# and queries 2^14 smaller (logits near zero).
+UNIT_FALLBACK = ["far_negative", "tile_spread", "tiny_logits"]
+
+
+@pytest.mark.parametrize("case", UNIT_FALLBACK)
+def test_scores_off_the_unit_scale(case):
+    wl = SEL["bf16_mid"]
+    q, k, _ = make_qkv(wl)
+    if case == "far_negative":
+        # q shifted by -1 and k by +16 in every dim: mu.kbar / sqrt(128) *
+        # log2(e) from about -175 to -110 (q keeps its structure, so k-means
+        # is as usual)
+        q = round_like(q - 1.0, wl.dtype)
+        k = round_like(k + 16.0, wl.dtype)
+    elif case == "tile_spread":
+        k = k.copy()
+        k[:, :, :128] = round_like(np.ldexp(k[:, :, :128], -20), wl.dtype)  # the first tile of 32 blocks
+    else:
+        q = round_like(np.ldexp(q, -14), wl.dtype)
+    op = oracle_problem(wl)
+    sc = oracle.ibcs_scores(q, k, op)
+    say(f"scores off the unit scale: {case}")
+    S, mu, w = ab.scores(to_dev(q, wl.dtype), to_dev(k, wl.dtype), lib_problem(wl))
+    torch.cuda.synchronize()
+    S, w = S.cpu().numpy(), w.cpu().numpy()
+    same = np.all(np.abs(w - sc["w"]) <= 1e-6, axis=1)
+    say(f"  k-means blocks with identical weights: {same.mean():.4f}")
+    assert same.mean() >= 0.99
+    rel = np.abs(S[same] - sc["S"][same]) / sc["S"][same]
+    say(f"  score rel err max {rel.max():.3e} mean {rel.mean():.3e}")
+    assert rel.max() <= 2e-3 and rel.mean() <= 2e-4
+    np.testing.assert_allclose(S.sum(axis=1), 1.0, rtol=1e-4)
 
 
 SAMPLER = [
