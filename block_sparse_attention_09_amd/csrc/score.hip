@@ -17,12 +17,18 @@
 //           each query block and written to S.
 // Two precisions of the dot products, both accumulated in fp32:
 //   * bf16 problems (kF16): one fp16 MFMA per k-step.  The key means come as
-//     fp16 scaled by a power of two per tile, the centroids are scaled by one
-//     power of two per work-group, both so that their largest magnitude lies
-//     in [2^14, 2^15): no overflow, 11 significant bits (finer than the bf16
-//     keys and queries they are averaged from).  The two scales multiply the
-//     logit inside the fma that already subtracts the running max (pass 1)
-//     or adds the centroid's offset (pass 2).
+//     fp16 scaled by a power of two per tile (largest magnitude in [1, 2)),
+//     and the centroids are scaled by one power of two per work-group: no
+//     overflow, 11 significant bits (finer than the bf16 keys and queries
+//     they are averaged from).  Usually (the unit scale) the work-group
+//     multiplies each tile by one exact fp16 power of two on its way to LDS
+//     and picks the centroids' power so that the MFMA yields the logit
+//     itself: pass 2 then starts its MFMAs from the centroid offsets and
+//     takes exp2 of their result, and pass 1 sums exp2(logit) against 0 and
+//     carries the tile's sum to its reference by one product.  Where the
+//     ranges do not allow that, the two scales multiply the logit inside
+//     the fma that also subtracts the running max (pass 1) or adds the
+//     centroid's offset (pass 2).
 //   * fp32 problems: both operands split into bf16 high and low parts
 //     (hi*hi + hi*lo + lo*hi, three MFMAs per k-step), which keeps the logits
 //     within ~2^-16 relative of fp32.
